@@ -1,0 +1,130 @@
+"""Plain fp64 CPU oracle for exact softmax attention.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+``bench.py``'s ``cpu_baseline`` leg may import this package.  It shares no
+code with the HIP library in ``io_aware_amd`` and never imports it; the
+library's product path never imports this package.
+
+Two parts:
+
+* ``attention`` -- the parity oracle: a C program (``attn_oracle.c``) that
+  computes, per query row, the three-pass safe softmax (max; sum of
+  exp(x - m); normalise) of the scaled scores and the weighted sum of value
+  rows, in IEEE double, with the causal mask M_ij = 0 for j <= i and -inf
+  otherwise, and returns O and LSE = m + ln(l).  Sources: "6. FlashAttention
+  分块逻辑" (lowentro.cn) sections 1.1 and 4.1; "9.4 FlashAttention 与
+  FlashMLA" (llm-fullstack-book) sections 9.4.2 and 9.4.5.
+* ``oracle.algorithms`` -- the pages' algorithms (one-pass online softmax,
+  blocked forward with deferred or per-step normalisation, split-KV partials
+  and their merge) in numpy fp64.  They exist to pin ``attention`` and each
+  other from several independent directions; they are not the parity oracle.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``attn_oracle.c`` into ``liboracle.so`` with gcc -O2 -fopenmp.
+
+    No -ffast-math: the oracle relies on IEEE double semantics.
+    """
+    global _lib
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-std=c99", "-Wall", "-shared", "-fPIC",
+           _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    _lib = None
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.oracle_attention_rows.restype = ctypes.c_int
+    lib.oracle_attention_rows.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_int64, ctypes.c_double, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_int64,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    lib.oracle_default_threads.restype = ctypes.c_int
+    lib.oracle_default_threads.argtypes = []
+    _lib = lib
+    return lib
+
+
+def default_threads() -> int:
+    """OpenMP threads the oracle uses when none are requested."""
+    return int(_load().oracle_default_threads())
+
+
+def _as_f32(x) -> np.ndarray:
+    if hasattr(x, "detach"):  # a torch tensor: widen exactly to float32 on the host
+        import torch
+        x = x.detach().to("cpu", torch.float32).numpy()
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    return a
+
+
+def attention(q, k, v, scale: float, causal: bool, rows=None, threads: int = 0):
+    """Exact attention in fp64 for [B, H, N, d] inputs.
+
+    ``q``, ``k``, ``v`` are float32-representable arrays (numpy or torch;
+    bf16/fp16 tensors are widened exactly).  ``scale`` is used as given
+    (pass the same float32 value the GPU receives).  ``rows`` selects flat
+    query rows ``(b*H + h)*Nq + i``; None means all rows.
+
+    Returns ``(out, lse)``: with ``rows`` None, out is [B, H, Nq, d] and lse
+    [B, H, Nq]; otherwise out is [len(rows), d] and lse [len(rows)].  Both
+    float64.
+    """
+    qa, ka, va = _as_f32(q), _as_f32(k), _as_f32(v)
+    if qa.ndim != 4 or ka.ndim != 4 or va.ndim != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, H, Nq, d = qa.shape
+    Nk = ka.shape[2]
+    if ka.shape != (B, H, Nk, d) or va.shape != ka.shape:
+        raise ValueError("shape mismatch: q %s k %s v %s" % (qa.shape, ka.shape, va.shape))
+    if rows is None:
+        nrows = B * H * Nq
+        rows_arr = None
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows = rows_arr.size
+    out = np.empty((nrows, d), dtype=np.float64)
+    lse = np.empty((nrows,), dtype=np.float64)
+    rc = _load().oracle_attention_rows(
+        qa.ctypes.data, ka.ctypes.data, va.ctypes.data,
+        B, H, Nq, Nk, d, float(scale), 1 if causal else 0,
+        None if rows_arr is None else rows_arr.ctypes.data, nrows,
+        out.ctypes.data, lse.ctypes.data, int(threads))
+    if rc != 0:
+        raise RuntimeError("oracle_attention_rows failed with code %d" % rc)
+    if rows is None:
+        return out.reshape(B, H, Nq, d), lse.reshape(B, H, Nq)
+    return out, lse
+
+
+def visible_keys(Nq: int, Nk: int, causal: bool, rows) -> np.ndarray:
+    """Number of keys each flat query row sees (top-left causal alignment)."""
+    i = np.asarray(rows, dtype=np.int64) % Nq
+    if not causal:
+        return np.full(i.shape, Nk, dtype=np.int64)
+    return np.minimum(i + 1, Nk)
