@@ -1,0 +1,186 @@
+"""Benchmark of the FlashAttention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|all]
+
+A step is one call of the forward (``fa_fwd``, or ``fa_fwd_splitkv`` for the
+decode workload) over one batch of seeded synthetic inputs already resident
+in device memory.  W untimed steps, then K timed steps bracketed by
+``torch.cuda.synchronize()``; each step is also bracketed by events on the
+stream the kernels run on, which gives the per-launch kernel time used for
+the roofline fraction.
+
+The default workload is causal bf16 prefill, B=8, H=16, N=4096, d=128.
+FLOPs follow the convention 4*B*H*Nq*Nk*d (the two contractions), halved
+under the causal mask; bytes are one read of Q, K, V and one write of O and
+LSE.  One JSON line per workload goes to stdout.
+
+The ``cpu_baseline`` leg times the fp64 oracle (test infrastructure) on a
+bounded sample of query rows of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+DEFAULT_WORKLOAD = "prefill_causal_bf16_b8h16_n4096_d128"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA
+PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector (packed)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+KERNEL_SOURCES = ["io_aware_amd/csrc/fa_prefill.hip", "io_aware_amd/csrc/fa_layout.h",
+                  "io_aware_amd/csrc/fa_decode.hip", "io_aware_amd/csrc/fa_f32.hip"]
+
+
+def workload_flops(w) -> float:
+    f = 4.0 * w.B * w.H * w.Nq * w.Nk * w.d
+    return f / 2 if w.causal else f
+
+
+def workload_bytes(w) -> float:
+    es = 4 if w.dtype == "f32" else 2
+    return float(es * w.B * w.H * (2 * w.Nq * w.d + 2 * w.Nk * w.d) + 4 * w.B * w.H * w.Nq)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary for
+    this workload, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, target_s: float):
+    """Time the fp64 oracle on a sample of rows; returns the baseline object."""
+    import numpy as np
+    import oracle
+    import fa_inputs
+    threads = len(os.sched_getaffinity(0))
+    qf, kf, vf = (t.float().numpy() for t in (q, k, v))   # exact widening, outside the timing
+    total_rows = w.B * w.H * w.Nq
+    n = min(total_rows, 256)
+    elapsed, flops, rows_done = 0.0, 0.0, 0
+    while True:
+        rows = np.sort(np.random.default_rng(n).choice(total_rows, size=n, replace=False)).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.attention(qf, kf, vf, w.scale, w.causal, rows=rows, threads=threads)
+        dt = time.perf_counter() - t0
+        vis = oracle.visible_keys(w.Nq, w.Nk, w.causal, rows)
+        elapsed, flops, rows_done = dt, float(4.0 * w.d * vis.sum()), n
+        if dt >= target_s or n >= total_rows:
+            break
+        n = min(total_rows, max(n * 2, int(n * target_s / max(dt, 1e-3) * 1.1)))
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d query rows (uniform, seed %d), %.1f s, fp64 three-pass oracle" % (
+                rows_done, total_rows, rows_done, elapsed)}
+
+
+def run_workload(name, steps, warmup, with_cpu, cpu_target_s):
+    import torch
+    import fa_inputs
+    import io_aware_amd as fa
+
+    w = fa_inputs.WORKLOADS[name]
+    q, k, v = fa_inputs.make_workload(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev).contiguous() for t in (q, k, v))
+    out = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    if w.num_splits:
+        ws = torch.empty(fa.fa_splitkv_workspace_bytes(w.B, w.H, w.Nq, w.d, w.num_splits), dtype=torch.uint8,
+                         device=dev)
+
+        def step():
+            fa.fa_fwd_splitkv(qd, kd, vd, w.num_splits, scale=w.scale, workspace=ws, out=out, lse=lse)
+    else:
+        def step():
+            fa.fa_fwd(qd, kd, vd, scale=w.scale, causal=w.causal, out=out, lse=lse)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in ev]
+    ms_per_step = wall * 1e3 / steps
+    kernel_ms = sum(launch_ms) / len(launch_ms)
+
+    flops = workload_flops(w)
+    nbytes = workload_bytes(w)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    if w.num_splits:
+        achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+    else:
+        peak = PEAK_FP32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+        achieved = flops / (kernel_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma" if w.dtype != "f32" else "alu", "achieved": achieved, "peak": peak,
+                "unit": "TFLOP/s", "frac": achieved / peak}
+    roof["traffic"] = measured_traffic(name)
+    rec = {
+        "metric": "attention fwd TFLOP/s (and % of MI355X bf16 MFMA/HBM roofline) per config",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded randn, cast with RNE)",
+        "config": {"workload": name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                   "causal": w.causal, "dtype": w.dtype, "q_sigma": w.q_sigma, "num_splits": w.num_splits,
+                   "flop_per_step": flops, "algorithmic_bytes_per_step": nbytes},
+        "roofline": roof,
+    }
+    if with_cpu:
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, cpu_target_s)
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this forward runs on one GPU; --gpus %d is not supported (use --gpus 1)" % args.gpus,
+              file=sys.stderr)
+        return 2
+    import fa_inputs
+    names = list(fa_inputs.WORKLOADS) if args.workload == "all" else [args.workload]
+    for i, name in enumerate(names):
+        rec = run_workload(name, args.steps, args.warmup,
+                           with_cpu=(not args.no_cpu_baseline) and (i == 0 or args.workload != "all"),
+                           cpu_target_s=args.cpu_seconds)
+        print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

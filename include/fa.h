@@ -1,0 +1,154 @@
+/*
+ * fa.h -- C ABI of the io_aware_amd FlashAttention forward for gfx950 (MI355X).
+ *
+ * The operation ("6. FlashAttention 分块逻辑" sections 1-6 and 11;
+ * "9.4 FlashAttention 与 FlashMLA" sections 9.4.2-9.4.5; "08. Triton Flash
+ * Attention" Steps 1-4): exact softmax attention
+ *
+ *     O = softmax(scale * Q K^T [+ causal mask]) V,   LSE = m + ln(l)
+ *
+ * computed per (batch, head) and Q row block, streaming K/V column blocks
+ * with the online softmax (running max m, running sum l, accumulator
+ * rescaled by exp(m_old - m_new)), so that the Nq x Nk score and probability
+ * matrices never reach device memory.  LSE is the per-row natural-log
+ * logsumexp of the scaled, masked scores (the statistic the backward pass
+ * rebuilds P from; "9.4 FlashAttention 与 FlashMLA", section 9.4.5).
+ *
+ * Layouts.  q: [B, H, Nq, d]; k, v: [B, H, Nk, d]; out: [B, H, Nq, d], all
+ * contiguous row-major (d fastest) in the element type ``dtype``.
+ * lse: [B, H, Nq] float32.  Accumulation and the m/l statistics are float32
+ * on every path; probabilities are rounded to the input type (nearest-even)
+ * before the P.V product, and O is rounded to the input type (nearest-even).
+ *
+ * Causal mask (``causal`` = 1): key j is visible to query i iff j <= i
+ * (top-left alignment, for any Nq and Nk; "6. FlashAttention 分块逻辑",
+ * section 4.1).  Out-of-range keys of a ragged last block are excluded
+ * (score -inf), never treated as score 0.
+ *
+ * Ownership.  Every pointer is device memory owned by the caller; the
+ * library never frees or retains it.  out and lse must not overlap q, k or
+ * v.  The library owns only the split-KV workspace cache of ``fa_fwd``
+ * (released by ``fa_release_workspace``).
+ *
+ * Asynchrony.  Every entry point enqueues its kernels on ``stream`` and
+ * returns; results are valid once the stream has completed that work.  A
+ * NULL stream is the device's default (null) stream.
+ *
+ * Errors.  Entry points return an ``fa_status``.  All arguments are checked
+ * on the host before any HIP call, so a rejected call has no device side
+ * effects.  ``fa_last_error`` returns a message for the calling thread's
+ * most recent failure.
+ */
+#ifndef IO_AWARE_AMD_FA_H
+#define IO_AWARE_AMD_FA_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of q, k, v and out (one type for all four). */
+typedef enum fa_dtype {
+    FA_F32 = 0,
+    FA_F16 = 1,
+    FA_BF16 = 2
+} fa_dtype;
+
+/* Status codes. */
+typedef enum fa_status {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = 1,  /* null pointer, a size < 1, scale not finite and > 0,
+                                causal not 0/1, overlapping outputs, num_splits < 1 */
+    FA_ERR_UNSUPPORTED = 2,  /* d not in {32, 64, 128}, unknown dtype, a pointer not
+                                16-byte aligned (lse: 4-byte), sizes past the index
+                                range, or a shape the entry point does not take */
+    FA_ERR_HIP = 3,          /* a HIP runtime call or kernel launch failed */
+    FA_ERR_WORKSPACE = 4     /* workspace missing, misaligned or too small */
+} fa_status;
+
+/*
+ * fa_fwd -- the forward pass.
+ *
+ * q, k, v, out: device pointers as described above; lse: device pointer to
+ * [B, H, Nq] float32, or NULL to skip writing LSE.  B, H, Nq, Nk >= 1;
+ * d in {32, 64, 128}; scale finite and > 0 (normally 1/sqrt(d)); causal 0 or
+ * 1; dtype an fa_dtype.
+ *
+ * Dispatch: Nq == 1 without the mask (single-token decode) runs the split-KV
+ * path ("6. FlashAttention 分块逻辑", section 11: K/V split into chunks that
+ * are processed independently, then merged by logsumexp weights) with
+ * fa_default_num_splits(Nk) chunks and a library-owned workspace kept per
+ * (device, stream); any other shape runs the tiled prefill kernel.
+ */
+int fa_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
+           int B, int H, int Nq, int Nk, int d, float scale, int causal,
+           int dtype, hipStream_t stream);
+
+/*
+ * fa_splitkv_workspace_bytes -- bytes of workspace fa_fwd_splitkv needs:
+ * B*H*Nq*num_splits*(d + 1) float32 values (each chunk's normalised partial
+ * output and its logsumexp), rounded up to 256 bytes.  Returns 0 for
+ * arguments outside the accepted ranges.
+ */
+size_t fa_splitkv_workspace_bytes(int B, int H, int Nq, int d, int num_splits);
+
+/*
+ * fa_fwd_splitkv -- single-token decode with an explicit number of K/V
+ * chunks ("6. FlashAttention 分块逻辑", section 11.3: stage one computes, per
+ * chunk, the local max, local sum and local output; stage two merges them).
+ *
+ * Chunk c covers keys [c*ceil(Nk/num_splits), min(Nk, (c+1)*ceil(Nk/num_splits))).
+ * Stage one stores, per chunk, lse_c = m_c + ln(l_c) and o~_c = o_c / l_c in
+ * float32; stage two forms LSE = logsumexp_c(lse_c) and O = sum_c
+ * exp(lse_c - LSE) o~_c.  An empty chunk gets weight 0.
+ *
+ * Nq must be 1 (FA_ERR_UNSUPPORTED otherwise); no causal mask.
+ * 1 <= num_splits <= 1024.  workspace: caller-owned device memory of at least
+ * fa_splitkv_workspace_bytes(B, H, Nq, d, num_splits) bytes, 16-byte aligned
+ * (FA_ERR_WORKSPACE otherwise); it must not be used by other work on the
+ * device while this call's kernels run.
+ */
+int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *out,
+                   float *lse, int B, int H, int Nq, int Nk, int d, float scale,
+                   int num_splits, void *workspace, size_t workspace_bytes,
+                   int dtype, hipStream_t stream);
+
+/*
+ * fa_default_num_splits -- chunk count fa_fwd uses for a decode call:
+ * ceil(Nk / 256) clamped to [1, 64] (8192 keys -> 32 chunks of 256).
+ * Returns 0 if Nk < 1.
+ */
+int fa_default_num_splits(int Nk);
+
+/*
+ * fa_release_workspace -- waits for the streams that used them, then frees
+ * the workspaces fa_fwd allocated.  Returns FA_OK or FA_ERR_HIP.
+ */
+int fa_release_workspace(void);
+
+/*
+ * fa_map_workgroup -- the prefill kernel's workgroup order, exposed so the
+ * host can check it: workgroup ``wg`` of ``BH * Tr`` processes (batch*head
+ * index *bh, Q row block *qblock).  Workgroups are spread over the 8 XCDs in
+ * dispatch order; the mapping gives each XCD whole heads so their K/V stay
+ * in that XCD's L2, and, under the causal mask, the longest (last) Q blocks
+ * of a head first.  Returns FA_OK, or FA_ERR_INVALID_ARG for wg out of range.
+ */
+int fa_map_workgroup(int wg, int BH, int Tr, int causal, int *bh, int *qblock);
+
+/* Static text for a status code. */
+const char *fa_status_string(int status);
+
+/* Message for the calling thread's most recent failed call ("" if none). */
+const char *fa_last_error(void);
+
+/* ABI version: 1. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IO_AWARE_AMD_FA_H */

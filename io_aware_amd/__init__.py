@@ -1,0 +1,182 @@
+"""io_aware_amd -- FlashAttention forward for MI355X (gfx950).
+
+A thin ctypes binding over ``libfa.so`` (the C ABI in ``include/fa.h``).  The
+functions keep the C names and only marshal arguments: torch tensors become
+device pointers and sizes, the current HIP stream becomes the ``stream``
+argument, and a non-zero status becomes an ``FAError``.  Every step of the
+computation runs in the library's HIP kernels; there is no other code path.
+PyTorch is used only for device memory and streams.
+
+The library is loaded at import; if it has not been built the import fails
+(build it with ``python -m io_aware_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_WORKSPACE = 0, 1, 2, 3, 4
+
+# every function include/fa.h declares, with its ctypes signature
+_SIGNATURES = {
+    "fa_fwd": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                              ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                              ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+    "fa_splitkv_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 5),
+    "fa_fwd_splitkv": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p,
+                                      ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]),
+    "fa_default_num_splits": (ctypes.c_int, [ctypes.c_int]),
+    "fa_release_workspace": (ctypes.c_int, []),
+    "fa_map_workgroup": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]),
+    "fa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "fa_last_error": (ctypes.c_char_p, []),
+    "fa_version": (ctypes.c_int, []),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("io_aware_amd: %s is not built; run `python -m io_aware_amd.build` "
+                          "(hipcc for gfx950) first" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib.fa_last_error().decode() or lib.fa_status_string(status).decode()
+        super().__init__("%s failed (%d): %s" % (where, status, msg))
+
+
+def _check(status: int, where: str) -> None:
+    if status != FA_OK:
+        raise FAError(status, where)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+    if t.dtype not in codes:
+        raise TypeError("unsupported dtype %s" % t.dtype)
+    return codes[t.dtype]
+
+
+def _stream_handle(t, stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _shapes(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous device tensor" % name)
+        if t.dtype != q.dtype:
+            raise TypeError("q, k and v must share one dtype")
+    return B, H, Nq, Nk, d
+
+
+def _outputs(q, out, lse, want_lse):
+    import torch
+    B, H, Nq, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    return out, lse
+
+
+def fa_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, return_lse=True, stream=None):
+    """O = softmax(scale * Q K^T [+ causal mask]) V and LSE for [B, H, N, d]
+    tensors.  Returns (out, lse) (lse None if ``return_lse`` is False and no
+    ``lse`` tensor is given).  ``scale`` defaults to 1/sqrt(d)."""
+    B, H, Nq, Nk, d = _shapes(q, k, v)
+    out, lse = _outputs(q, out, lse, return_lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check(lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d, float(scale),
+                      1 if causal else 0, _dtype_code(q), _stream_handle(q, stream)), "fa_fwd")
+    return out, lse
+
+
+def fa_splitkv_workspace_bytes(B, H, Nq, d, num_splits) -> int:
+    return int(lib.fa_splitkv_workspace_bytes(B, H, Nq, d, num_splits))
+
+
+def fa_fwd_splitkv(q, k, v, num_splits, scale=None, workspace=None, out=None, lse=None, return_lse=True,
+                   stream=None):
+    """Single-token decode (Nq == 1) with ``num_splits`` K/V chunks merged by
+    logsumexp weights.  ``workspace`` is a device tensor of at least
+    ``fa_splitkv_workspace_bytes`` bytes (allocated here if None)."""
+    import torch
+    B, H, Nq, Nk, d = _shapes(q, k, v)
+    out, lse = _outputs(q, out, lse, return_lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = fa_splitkv_workspace_bytes(B, H, Nq, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d, float(scale),
+                              int(num_splits), _ptr(workspace), ws_bytes, _dtype_code(q),
+                              _stream_handle(q, stream)), "fa_fwd_splitkv")
+    return out, lse
+
+
+def fa_default_num_splits(Nk: int) -> int:
+    return int(lib.fa_default_num_splits(Nk))
+
+
+def fa_release_workspace() -> None:
+    _check(lib.fa_release_workspace(), "fa_release_workspace")
+
+
+def fa_map_workgroup(wg: int, BH: int, Tr: int, causal: bool):
+    bh, qb = ctypes.c_int(-1), ctypes.c_int(-1)
+    _check(lib.fa_map_workgroup(wg, BH, Tr, 1 if causal else 0, ctypes.byref(bh), ctypes.byref(qb)),
+           "fa_map_workgroup")
+    return bh.value, qb.value
+
+
+def fa_status_string(status: int) -> str:
+    return lib.fa_status_string(status).decode()
+
+
+def fa_last_error() -> str:
+    return lib.fa_last_error().decode()
+
+
+def fa_version() -> int:
+    return int(lib.fa_version())
+
+
+__all__ = ["fa_fwd", "fa_fwd_splitkv", "fa_splitkv_workspace_bytes", "fa_default_num_splits",
+           "fa_release_workspace", "fa_map_workgroup", "fa_status_string", "fa_last_error", "fa_version",
+           "FAError", "FA_F32", "FA_F16", "FA_BF16", "lib", "LIB_PATH"]

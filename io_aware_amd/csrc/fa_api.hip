@@ -1,0 +1,232 @@
+// fa_api.hip -- the C ABI declared in include/fa.h: argument checks (all on
+// the host, before any HIP call), dispatch to the kernels, the decode
+// workspace cache, and error reporting.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "fa.h"
+#include "fa_internal.h"
+#include "fa_layout.h"
+
+namespace {
+
+constexpr int kMaxSplits = 1024;
+constexpr double kLog2e = 1.4426950408889634073599;
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string &msg) {
+    g_last_error = msg;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return FA_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+size_t element_size(int dtype) { return dtype == FA_F32 ? 4 : 2; }
+
+// Checks shared by every forward entry point.  Returns FA_OK or the status
+// to return, with the message set.
+int check_common(const void *q, const void *k, const void *v, const void *out, const float *lse, int B, int H,
+                 int Nq, int Nk, int d, float scale, int dtype) {
+    if (!q || !k || !v || !out) return fail(FA_ERR_INVALID_ARG, "q, k, v and out must be non-null");
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1)
+        return fail(FA_ERR_INVALID_ARG, "B, H, Nq, Nk and d must all be >= 1");
+    if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+    if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16)
+        return fail(FA_ERR_UNSUPPORTED, "dtype must be FA_F32 (0), FA_F16 (1) or FA_BF16 (2)");
+    if (d != 32 && d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "d must be 32, 64 or 128");
+    if ((int64_t)B * H > INT32_MAX || (int64_t)Nq * d > INT32_MAX || (int64_t)Nk * d > INT32_MAX)
+        return fail(FA_ERR_UNSUPPORTED, "B*H, Nq*d and Nk*d must each fit in 31 bits");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+        return fail(FA_ERR_UNSUPPORTED, "q, k, v and out must be 16-byte aligned");
+    if (lse && !aligned(lse, 4)) return fail(FA_ERR_UNSUPPORTED, "lse must be 4-byte aligned");
+    const size_t es = element_size(dtype);
+    const size_t bh = (size_t)B * H;
+    const size_t q_bytes = bh * Nq * d * es, kv_bytes = bh * Nk * d * es;
+    const size_t lse_bytes = bh * Nq * sizeof(float);
+    if (overlaps(out, q_bytes, q, q_bytes) || overlaps(out, q_bytes, k, kv_bytes) ||
+        overlaps(out, q_bytes, v, kv_bytes))
+        return fail(FA_ERR_INVALID_ARG, "out overlaps q, k or v");
+    if (lse && (overlaps(lse, lse_bytes, q, q_bytes) || overlaps(lse, lse_bytes, k, kv_bytes) ||
+                overlaps(lse, lse_bytes, v, kv_bytes) || overlaps(lse, lse_bytes, out, q_bytes)))
+        return fail(FA_ERR_INVALID_ARG, "lse overlaps q, k, v or out");
+    return FA_OK;
+}
+
+int hip_status(hipError_t err, const char *what) {
+    if (err == hipSuccess) return ok();
+    return fail(FA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(err));
+}
+
+size_t workspace_bytes(int B, int H, int Nq, int d, int S) {
+    const size_t floats = (size_t)B * H * Nq * S * ((size_t)d + 1);
+    return (floats * sizeof(float) + 255) / 256 * 256;
+}
+
+// Prefill tile shape: the default, or FA_PREFILL_SHAPE (0, 1, 2) for sweeps.
+int prefill_shape() {
+    const char *env = std::getenv("FA_PREFILL_SHAPE");
+    if (env && env[0] >= '0' && env[0] < '0' + fa::kNumPrefillShapes && env[1] == '\0') return env[0] - '0';
+    return fa::kShapeW4Q32;
+}
+
+// Library-owned decode workspaces, one per (device, stream).
+struct Workspace {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+int get_workspace(size_t need, hipStream_t stream, void **out) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return hip_status(err, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace &w = g_ws[std::make_pair(dev, stream)];
+    if (w.bytes < need) {
+        if (w.ptr) {
+            // earlier work on this stream may still read the old buffer
+            err = hipStreamSynchronize(stream);
+            if (err != hipSuccess) return hip_status(err, "hipStreamSynchronize");
+            err = hipFree(w.ptr);
+            w.ptr = nullptr;
+            w.bytes = 0;
+            if (err != hipSuccess) return hip_status(err, "hipFree");
+        }
+        err = hipMalloc(&w.ptr, need);
+        if (err != hipSuccess) {
+            w.ptr = nullptr;
+            return hip_status(err, "hipMalloc(workspace)");
+        }
+        w.bytes = need;
+    }
+    *out = w.ptr;
+    return FA_OK;
+}
+
+int run_splitkv(const void *q, const void *k, const void *v, void *out, float *lse, int B, int H, int Nk, int d,
+                float scale, int S, void *ws, int dtype, hipStream_t stream) {
+    const float sl = (float)((double)scale * kLog2e);
+    return hip_status(fa::launch_splitkv(dtype, d, q, k, v, out, lse, B * H, Nk, sl, S, ws, stream),
+                      "split-KV launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void *q, const void *k, const void *v, void *out, float *lse, int B, int H, int Nq, int Nk, int d,
+           float scale, int causal, int dtype, hipStream_t stream) {
+    int st = check_common(q, k, v, out, lse, B, H, Nq, Nk, d, scale, dtype);
+    if (st != FA_OK) return st;
+    if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+
+    if (Nq == 1 && !causal && dtype != FA_F32) {
+        const int S = fa_default_num_splits(Nk);
+        void *ws = nullptr;
+        st = get_workspace(workspace_bytes(B, H, 1, d, S), stream, &ws);
+        if (st != FA_OK) return st;
+        return run_splitkv(q, k, v, out, lse, B, H, Nk, d, scale, S, ws, dtype, stream);
+    }
+    const float sl = (float)((double)scale * kLog2e);
+    if (dtype == FA_F32)
+        return hip_status(fa::launch_prefill_f32(d, causal == 1, q, k, v, out, lse, B * H, Nq, Nk, sl, stream),
+                          "fp32 prefill launch");
+    return hip_status(
+        fa::launch_prefill(dtype, d, causal == 1, prefill_shape(), q, k, v, out, lse, B * H, Nq, Nk, sl, stream),
+        "prefill launch");
+}
+
+size_t fa_splitkv_workspace_bytes(int B, int H, int Nq, int d, int num_splits) {
+    if (B < 1 || H < 1 || Nq < 1 || d < 1 || num_splits < 1 || num_splits > kMaxSplits) return 0;
+    return workspace_bytes(B, H, Nq, d, num_splits);
+}
+
+int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *out, float *lse, int B, int H, int Nq, int Nk,
+                   int d, float scale, int num_splits, void *workspace, size_t ws_bytes, int dtype,
+                   hipStream_t stream) {
+    int st = check_common(q, k, v, out, lse, B, H, Nq, Nk, d, scale, dtype);
+    if (st != FA_OK) return st;
+    if (num_splits < 1 || num_splits > kMaxSplits)
+        return fail(FA_ERR_INVALID_ARG, "num_splits must be in [1, 1024]");
+    if (Nq != 1) return fail(FA_ERR_UNSUPPORTED, "the split-KV path takes Nq == 1 (single-token decode)");
+    if (dtype == FA_F32) return fail(FA_ERR_UNSUPPORTED, "the split-KV path takes fp16 or bf16");
+    const size_t need = workspace_bytes(B, H, Nq, d, num_splits);
+    if (!workspace || !aligned(workspace, 16) || ws_bytes < need)
+        return fail(FA_ERR_WORKSPACE, "workspace must be 16-byte aligned and hold fa_splitkv_workspace_bytes() = " +
+                                          std::to_string(need) + " bytes");
+    const size_t es = element_size(dtype);
+    const size_t bh = (size_t)B * H;
+    if (overlaps(workspace, need, q, bh * d * es) || overlaps(workspace, need, k, bh * Nk * d * es) ||
+        overlaps(workspace, need, v, bh * Nk * d * es) || overlaps(workspace, need, out, bh * d * es) ||
+        (lse && overlaps(workspace, need, lse, bh * sizeof(float))))
+        return fail(FA_ERR_WORKSPACE, "workspace overlaps an input or output");
+    return run_splitkv(q, k, v, out, lse, B, H, Nk, d, scale, num_splits, workspace, dtype, stream);
+}
+
+int fa_default_num_splits(int Nk) {
+    if (Nk < 1) return 0;
+    int s = (Nk + 255) / 256;
+    return s < 1 ? 1 : (s > 64 ? 64 : s);
+}
+
+int fa_release_workspace(void) {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    int status = FA_OK;
+    int prev = -1;
+    const bool have_prev = hipGetDevice(&prev) == hipSuccess;
+    for (auto &kv : g_ws) {
+        if (!kv.second.ptr) continue;
+        hipError_t err = hipSetDevice(kv.first.first);
+        if (err == hipSuccess) err = hipDeviceSynchronize();
+        if (err == hipSuccess) err = hipFree(kv.second.ptr);
+        if (err != hipSuccess) status = hip_status(err, "releasing a workspace");
+        kv.second.ptr = nullptr;
+        kv.second.bytes = 0;
+    }
+    g_ws.clear();
+    if (have_prev) (void)hipSetDevice(prev);
+    return status == FA_OK ? ok() : status;
+}
+
+int fa_map_workgroup(int wg, int BH, int Tr, int causal, int *bh, int *qblock) {
+    if (BH < 1 || Tr < 1 || (int64_t)BH * Tr > INT32_MAX || wg < 0 || wg >= BH * Tr || !bh || !qblock)
+        return fail(FA_ERR_INVALID_ARG, "wg must be in [0, BH*Tr) with BH, Tr >= 1 and non-null outputs");
+    fa::layout::map_workgroup(wg, BH, Tr, causal != 0, *bh, *qblock);
+    return ok();
+}
+
+const char *fa_status_string(int status) {
+    switch (status) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported shape, type or alignment";
+        case FA_ERR_HIP: return "FA_ERR_HIP: HIP runtime error";
+        case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+        default: return "unknown fa_status";
+    }
+}
+
+const char *fa_last_error(void) { return g_last_error.c_str(); }
+
+int fa_version(void) { return 1; }
+
+}  // extern "C"

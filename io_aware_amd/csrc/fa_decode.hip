@@ -1,0 +1,286 @@
+// fa_decode.hip -- split-KV forward for single-token decode on gfx950.
+//
+// Method ("6. FlashAttention 分块逻辑" section 11, FlashDecoding): with one
+// query row the Q-block loop has a single block, so the K/V sequence is cut
+// into chunks that separate workgroups process in parallel.  Stage one (per
+// chunk c): scores s = scale * q K_c^T, local max m_c, p = exp(s - m_c),
+// local sum l_c, local output o_c = p V_c; it stores lse_c = m_c + ln l_c and
+// the normalised o~_c = o_c / l_c in float32.  Stage two merges the chunks:
+// LSE = logsumexp_c lse_c and O = sum_c exp(lse_c - LSE) o~_c, which is the
+// same function as the page's sequential (m, l, o) merge.
+//
+// The work is bound by HBM bandwidth (one pass over K and V, about 1 FLOP per
+// byte), so the design is about bytes in flight, not arithmetic:
+//  * a 256-thread workgroup reads its chunk as 16-byte loads; CH = d/8
+//    consecutive lanes cover one key row (256 contiguous bytes at d = 128),
+//    so every load instruction reads whole rows;
+//  * each thread issues the loads of U = 8 keys of K and of V before it uses
+//    any (8 KB per wave in flight per round);
+//  * partial dot products are summed across the CH lanes of a row with
+//    lane exchanges; each thread keeps an online (m, l, o) over its keys
+//    and the workgroup merges the KL = 256/CH key lanes through LDS at the
+//    end, so the only HBM traffic besides K and V is the chunk's d + 1
+//    floats.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLn2d = 0.693147180559945309417f;
+constexpr float kLog2e = 1.442695040888963407360f;
+constexpr int kSplitThreads = 256;
+constexpr int kKeysPerRound = 8;   // U: keys per thread per round
+constexpr int kMaxSplits = 1024;
+
+struct SplitArgs {
+    const void *q;
+    const void *k;
+    const void *v;
+    float *ws_o;    // [BH, S, D] normalised chunk outputs
+    float *ws_lse;  // [BH, S] chunk logsumexp (natural log)
+    int Nk;
+    int S;
+    int chunk;      // keys per chunk = ceil(Nk / S)
+    float scale_log2;
+};
+
+struct CombineArgs {
+    const float *ws_o;
+    const float *ws_lse;
+    void *out;
+    float *lse;
+    int rows;
+    int S;
+};
+
+// 2-byte element (bf16 or fp16) -> float
+template <typename T>
+__device__ __forceinline__ float lo_to_f32(uint32_t w);
+template <typename T>
+__device__ __forceinline__ float hi_to_f32(uint32_t w);
+
+template <>
+__device__ __forceinline__ float lo_to_f32<__bf16>(uint32_t w) { return __uint_as_float(w << 16); }
+template <>
+__device__ __forceinline__ float hi_to_f32<__bf16>(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+template <>
+__device__ __forceinline__ float lo_to_f32<_Float16>(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+template <>
+__device__ __forceinline__ float hi_to_f32<_Float16>(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kSplitThreads) void splitkv_partial_kernel(SplitArgs a) {
+    constexpr int NT = kSplitThreads;
+    constexpr int CH = D / 8;   // lanes per key row (16 bytes each)
+    constexpr int KL = NT / CH; // key lanes
+    constexpr int U = kKeysPerRound;
+    static_assert(CH <= 64 && (CH & (CH - 1)) == 0, "row lanes must be a power of two within a wave");
+
+    __shared__ float sm_m[KL];
+    __shared__ float sm_l[KL];
+    __shared__ float sm_o[KL * D];
+
+    const int tid = threadIdx.x;
+    const int dc = tid % CH;
+    const int kl = tid / CH;
+    const int bh = blockIdx.x / a.S;
+    const int cidx = blockIdx.x - bh * a.S;
+    const int Nk = a.Nk;
+    const int kbeg = min(Nk, cidx * a.chunk);
+    const int kend = min(Nk, kbeg + a.chunk);
+    const float c = a.scale_log2;
+
+    const T *kp = static_cast<const T *>(a.k) + (size_t)bh * Nk * D + dc * 8;
+    const T *vp = static_cast<const T *>(a.v) + (size_t)bh * Nk * D + dc * 8;
+    const u32x4 qraw = *reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.q) + (size_t)bh * D + dc * 8);
+    float qv[8];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        qv[2 * w] = lo_to_f32<T>(qraw[w]);
+        qv[2 * w + 1] = hi_to_f32<T>(qraw[w]);
+    }
+
+    float m_run = -__builtin_inff();  // exp2 domain
+    float l_run = 0.f;
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+
+    for (int base = kbeg; base < kend; base += KL * U) {
+        u32x4 kx[U], vx[U];
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const int key = base + kl + KL * i;
+            kx[i] = u32x4{0u, 0u, 0u, 0u};
+            if (key < kend) kx[i] = *reinterpret_cast<const u32x4 *>(kp + (size_t)key * D);
+        }
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const int key = base + kl + KL * i;
+            vx[i] = u32x4{0u, 0u, 0u, 0u};
+            if (key < kend) vx[i] = *reinterpret_cast<const u32x4 *>(vp + (size_t)key * D);
+        }
+        float s[U];
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            float dot = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                dot = __builtin_fmaf(qv[2 * w], lo_to_f32<T>(kx[i][w]), dot);
+                dot = __builtin_fmaf(qv[2 * w + 1], hi_to_f32<T>(kx[i][w]), dot);
+            }
+#pragma unroll
+            for (int msk = CH / 2; msk > 0; msk >>= 1) dot += __shfl_xor(dot, msk);
+            const int key = base + kl + KL * i;
+            s[i] = (key < kend) ? dot * c : -__builtin_inff();
+            mx = __builtin_fmaxf(mx, s[i]);
+        }
+        const float m_new = __builtin_fmaxf(m_run, mx);
+        const float alpha = (m_new == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        const float msub = (m_new == -__builtin_inff()) ? 0.f : m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] *= alpha;
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const float p = __builtin_amdgcn_exp2f(s[i] - msub);
+            l_run += p;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                o[2 * w] = __builtin_fmaf(p, lo_to_f32<T>(vx[i][w]), o[2 * w]);
+                o[2 * w + 1] = __builtin_fmaf(p, hi_to_f32<T>(vx[i][w]), o[2 * w + 1]);
+            }
+        }
+        m_run = m_new;
+    }
+
+    // merge the KL key lanes of the workgroup
+    if (dc == 0) {
+        sm_m[kl] = m_run;
+        sm_l[kl] = l_run;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sm_o[kl * D + dc * 8 + e] = o[e];
+    __syncthreads();
+
+    const size_t slot = (size_t)bh * a.S + cidx;
+    for (int dim = tid; dim < D; dim += NT) {
+        float M = -__builtin_inff();
+        for (int j = 0; j < KL; ++j) M = __builtin_fmaxf(M, sm_m[j]);
+        float L = 0.f, O = 0.f;
+        if (M != -__builtin_inff()) {
+            for (int j = 0; j < KL; ++j) {
+                const float w = __builtin_amdgcn_exp2f(sm_m[j] - M);  // exp2(-inf) = 0 for empty lanes
+                L = __builtin_fmaf(sm_l[j], w, L);
+                O = __builtin_fmaf(sm_o[j * D + dim], w, O);
+            }
+        }
+        a.ws_o[slot * D + dim] = (L > 0.f) ? O / L : 0.f;
+        if (dim == 0) a.ws_lse[slot] = (L > 0.f) ? (M + __builtin_amdgcn_logf(L)) * kLn2d : -__builtin_inff();
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x) {
+    return (T)x;  // round to nearest even
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void splitkv_combine_kernel(CombineArgs a) {
+    __shared__ float wts[4][kMaxSplits];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int row = blockIdx.x * 4 + wave;
+    const bool valid = row < a.rows;  // wave-uniform
+    const int S = a.S;
+    float LSE = 0.f;
+    if (valid) {
+        const float *lse_c = a.ws_lse + (size_t)row * S;
+        float M = -__builtin_inff();
+        for (int c = lane; c < S; c += 64) M = __builtin_fmaxf(M, lse_c[c]);
+#pragma unroll
+        for (int msk = 32; msk > 0; msk >>= 1) M = __builtin_fmaxf(M, __shfl_xor(M, msk));
+        float L = 0.f;
+        for (int c = lane; c < S; c += 64) L += __builtin_amdgcn_exp2f((lse_c[c] - M) * kLog2e);
+#pragma unroll
+        for (int msk = 32; msk > 0; msk >>= 1) L += __shfl_xor(L, msk);
+        LSE = M + __builtin_amdgcn_logf(L) * kLn2d;
+        for (int c = lane; c < S; c += 64) wts[wave][c] = __builtin_amdgcn_exp2f((lse_c[c] - LSE) * kLog2e);
+    }
+    __syncthreads();  // reached by every wave
+    if (!valid) return;
+
+    T *op = static_cast<T *>(a.out) + (size_t)row * D;
+    const float *oc = a.ws_o + (size_t)row * S * D;
+    for (int dim = lane; dim < D; dim += 64) {
+        float acc = 0.f;
+        for (int c = 0; c < S; ++c) acc = __builtin_fmaf(wts[wave][c], oc[(size_t)c * D + dim], acc);
+        op[dim] = from_f32<T>(acc);
+    }
+    if (lane == 0 && a.lse != nullptr) a.lse[row] = LSE;
+}
+
+template <typename T, int D>
+hipError_t launch_splitkv_typed(const void *q, const void *k, const void *v, void *out, float *lse, int BH,
+                                int Nk, float sl, int S, void *workspace, hipStream_t stream) {
+    float *ws_o = static_cast<float *>(workspace);
+    float *ws_lse = ws_o + (size_t)BH * S * D;
+    SplitArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.ws_o = ws_o;
+    a.ws_lse = ws_lse;
+    a.Nk = Nk;
+    a.S = S;
+    a.chunk = (Nk + S - 1) / S;
+    a.scale_log2 = sl;
+    const long long nwg = (long long)BH * S;
+    if (nwg > 0x7fffffffLL || S > kMaxSplits) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((splitkv_partial_kernel<T, D>), dim3((unsigned)nwg), dim3(kSplitThreads), 0, stream, a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    CombineArgs b;
+    b.ws_o = ws_o;
+    b.ws_lse = ws_lse;
+    b.out = out;
+    b.lse = lse;
+    b.rows = BH;
+    b.S = S;
+    hipLaunchKernelGGL((splitkv_combine_kernel<T, D>), dim3((BH + 3) / 4), dim3(256), 0, stream, b);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_splitkv_d(int d, const void *q, const void *k, const void *v, void *out, float *lse, int BH,
+                            int Nk, float sl, int S, void *ws, hipStream_t stream) {
+    switch (d) {
+        case 32: return launch_splitkv_typed<T, 32>(q, k, v, out, lse, BH, Nk, sl, S, ws, stream);
+        case 64: return launch_splitkv_typed<T, 64>(q, k, v, out, lse, BH, Nk, sl, S, ws, stream);
+        case 128: return launch_splitkv_typed<T, 128>(q, k, v, out, lse, BH, Nk, sl, S, ws, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_splitkv(int dtype, int d, const void *q, const void *k, const void *v, void *out, float *lse,
+                          int BH, int Nk, float scale_log2, int num_splits, void *workspace, hipStream_t stream) {
+    if (dtype == 2)
+        return launch_splitkv_d<__bf16>(d, q, k, v, out, lse, BH, Nk, scale_log2, num_splits, workspace, stream);
+    if (dtype == 1)
+        return launch_splitkv_d<_Float16>(d, q, k, v, out, lse, BH, Nk, scale_log2, num_splits, workspace, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace fa

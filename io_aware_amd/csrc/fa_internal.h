@@ -1,0 +1,43 @@
+// fa_internal.h -- launchers shared between the C ABI (fa_api.hip) and the
+// kernel translation units.  Every launcher assumes its arguments were
+// validated by the ABI layer and only enqueues work on ``stream``.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+// Prefill tile shapes the library is built with.  A shape is (waves per
+// workgroup, queries per wave, keys per K/V tile); queries per workgroup
+// (Br) = waves * queries per wave.
+enum PrefillShape {
+    kShapeW4Q32 = 0,   // 4 waves x 32 queries = Br 128, Bc 64
+    kShapeW4Q64 = 1,   // 4 waves x 64 queries = Br 256, Bc 64
+    kShapeW2Q64 = 2,   // 2 waves x 64 queries = Br 128, Bc 64
+    kNumPrefillShapes = 3
+};
+
+// Queries per workgroup (Br) of a prefill shape.
+int prefill_block_rows(int shape);
+
+// bf16 / fp16 tiled forward (MFMA).  dtype is FA_F16 or FA_BF16; d in
+// {32, 64, 128}.  scale_log2 = scale * log2(e).
+hipError_t launch_prefill(int dtype, int d, bool causal, int shape,
+                          const void *q, const void *k, const void *v,
+                          void *out, float *lse, int BH, int Nq, int Nk,
+                          float scale_log2, hipStream_t stream);
+
+// float32 tiled forward (vector ALU), Br = Bc = 64.
+hipError_t launch_prefill_f32(int d, bool causal, const void *q, const void *k,
+                              const void *v, void *out, float *lse, int BH,
+                              int Nq, int Nk, float scale_log2, hipStream_t stream);
+
+// Split-KV decode: stage one (per chunk partials into the workspace) then
+// stage two (logsumexp-weighted combine).  dtype FA_F16 or FA_BF16; Nq == 1.
+hipError_t launch_splitkv(int dtype, int d, const void *q, const void *k,
+                          const void *v, void *out, float *lse, int BH, int Nk,
+                          float scale_log2, int num_splits, void *workspace,
+                          hipStream_t stream);
+
+}  // namespace fa

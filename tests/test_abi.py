@@ -1,0 +1,169 @@
+"""The C ABI on the host: the library loads, exports every function
+include/fa.h declares, and rejects every invalid argument before any HIP
+call (so these run without a GPU), plus the host-side planning logic.
+
+Pointers passed here are fake, 16-byte aligned addresses: every call below is
+built so that validation rejects it, and validation runs before the library
+touches HIP or memory.
+"""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def fa():
+    lib_path = os.path.join(ROOT, "io_aware_amd", "libfa.so")
+    if not os.path.exists(lib_path):        # build once, without importing the package
+        import importlib.util
+        spec = importlib.util.spec_from_file_location("fa_build", os.path.join(ROOT, "io_aware_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
+    import io_aware_amd
+    return io_aware_amd
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("fa_fwd", "fa_fwd_splitkv", "fa_splitkv_workspace_bytes", "fa_status_string",
+                 "fa_last_error", "fa_release_workspace", "fa_default_num_splits", "fa_map_workgroup"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(fa):
+    names = declared_functions()
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = set(line.split()[-1] for line in out.stdout.splitlines() if line.strip())
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert getattr(fa.lib, n) is not None
+    # the binding wraps every declared function under the same name
+    for n in names:
+        assert callable(getattr(fa, n)), n
+
+
+def test_version_and_status_strings(fa):
+    assert fa.fa_version() == 1
+    for code in range(5):
+        assert fa.fa_status_string(code).startswith(["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED",
+                                                     "FA_ERR_HIP", "FA_ERR_WORKSPACE"][code])
+    assert "unknown" in fa.fa_status_string(99)
+
+
+# fake device addresses: 16-byte aligned, far apart
+Q, K, V, O, L, W = (0x10000000 * i for i in range(1, 7))
+GOOD = dict(q=Q, k=K, v=V, out=O, lse=L, B=2, H=4, Nq=100, Nk=100, d=64, scale=0.125, causal=0, dtype=2)
+
+
+def call_fwd(fa, **over):
+    a = dict(GOOD)
+    a.update(over)
+    return fa.lib.fa_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"],
+                         a["scale"], a["causal"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(out=None), 1),
+    (dict(B=0), 1), (dict(H=-1), 1), (dict(Nq=0), 1), (dict(Nk=0), 1), (dict(d=0), 1),
+    (dict(scale=0.0), 1), (dict(scale=-0.5), 1), (dict(scale=math.nan), 1), (dict(scale=math.inf), 1),
+    (dict(causal=2), 1), (dict(causal=-1), 1),
+    (dict(dtype=3), 2), (dict(dtype=-1), 2),
+    (dict(d=48), 2), (dict(d=256), 2), (dict(d=16), 2),
+    (dict(q=Q + 8), 2), (dict(out=O + 4), 2), (dict(lse=L + 2), 2),
+    (dict(Nq=1 << 26, d=64), 2),
+    (dict(out=Q + 64), 1), (dict(lse=K + 1024), 1), (dict(lse=O + 16), 1),
+])
+def test_fwd_rejects_invalid_arguments(fa, over, code):
+    assert call_fwd(fa, **over) == code
+    assert fa.fa_last_error() != ""
+
+
+def test_error_message_is_per_thread(fa):
+    import threading
+    assert call_fwd(fa, d=48) == 2
+    seen = {}
+
+    def other():
+        seen["msg"] = fa.fa_last_error()
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == ""
+    assert "d must be" in fa.fa_last_error()
+
+
+def call_split(fa, S=32, ws=W, ws_bytes=None, **over):
+    a = dict(GOOD, Nq=1, Nk=8192, d=128)
+    a.update(over)
+    if ws_bytes is None:
+        ws_bytes = fa.fa_splitkv_workspace_bytes(a["B"], a["H"], a["Nq"], a["d"], S)
+    return fa.lib.fa_fwd_splitkv(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"], a["Nq"], a["Nk"],
+                                 a["d"], a["scale"], S, ws, ws_bytes, a["dtype"], None)
+
+
+def test_splitkv_rejects_invalid_arguments(fa):
+    assert call_split(fa, S=0) == 1
+    assert call_split(fa, S=1025) == 1
+    assert call_split(fa, q=None) == 1
+    assert call_split(fa, Nq=2) == 2                   # decode only
+    assert call_split(fa, dtype=0) == 2                # fp16 / bf16 only
+    assert call_split(fa, ws=None) == 4
+    assert call_split(fa, ws=W + 8) == 4
+    assert call_split(fa, ws_bytes=1024) == 4
+    assert call_split(fa, ws=K) == 4                   # overlaps k
+
+
+def test_workspace_bytes(fa):
+    n = fa.fa_splitkv_workspace_bytes(16, 32, 1, 128, 32)
+    assert n == 16 * 32 * 32 * 129 * 4                  # already a multiple of 256
+    assert fa.fa_splitkv_workspace_bytes(1, 1, 1, 64, 3) == 1024   # 780 bytes rounded up to 256
+    assert fa.fa_splitkv_workspace_bytes(0, 1, 1, 64, 3) == 0
+    assert fa.fa_splitkv_workspace_bytes(1, 1, 1, 64, 0) == 0
+    assert fa.fa_splitkv_workspace_bytes(1, 1, 1, 64, 2000) == 0
+
+
+def test_default_num_splits(fa):
+    assert fa.fa_default_num_splits(8192) == 32          # 32 chunks of 256 keys
+    assert fa.fa_default_num_splits(1) == 1
+    assert fa.fa_default_num_splits(257) == 2
+    assert fa.fa_default_num_splits(10 ** 6) == 64
+    assert fa.fa_default_num_splits(0) == 0
+
+
+@pytest.mark.parametrize("BH,Tr", [(128, 32), (32, 128), (16, 8), (3, 5), (1, 1), (512, 1)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_workgroup_order_is_a_bijection(fa, BH, Tr, causal):
+    seen = set()
+    for wg in range(BH * Tr):
+        bh, qb = fa.fa_map_workgroup(wg, BH, Tr, causal)
+        assert 0 <= bh < BH and 0 <= qb < Tr
+        seen.add((bh, qb))
+    assert len(seen) == BH * Tr
+    with pytest.raises(fa.FAError):
+        fa.fa_map_workgroup(BH * Tr, BH, Tr, causal)
+
+
+def test_workgroup_order_groups_heads_by_xcd(fa):
+    # 128 heads x 32 blocks: XCD x (= wg % 8) gets heads 16x .. 16x+15
+    BH, Tr = 128, 32
+    for wg in range(0, BH * Tr, 37):
+        bh, _ = fa.fa_map_workgroup(wg, BH, Tr, True)
+        assert bh // 16 == wg % 8
+    # causal: the first workgroup of a head takes its last (longest) block
+    assert fa.fa_map_workgroup(0, BH, Tr, True) == (0, Tr - 1)
+    assert fa.fa_map_workgroup(0, BH, Tr, False) == (0, 0)

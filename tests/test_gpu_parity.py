@@ -1,0 +1,252 @@
+"""GPU parity: the HIP path against the fp64 oracle on identical seeded inputs.
+
+Every call goes through the C ABI (``io_aware_amd`` is a ctypes binding).
+Tolerances on O and LSE (absolute, after widening the GPU outputs to fp64):
+
+* float32 path: max |O - O_ref| <= 1e-5;
+* fp16 / bf16 paths: max |O - O_ref| <= 2e-2 and mean |O - O_ref| <= 2e-3;
+* LSE: max |LSE - LSE_ref| <= 1e-3 on every path.
+
+Small and medium cases are compared in full; the full-size workloads (the
+same launch configuration bench.py times) are compared on a deterministic
+sample of rows that includes first/last rows and tile boundaries.
+"""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import fa_inputs
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-5, None), "f16": (2e-2, 2e-3), "bf16": (2e-2, 2e-3)}
+LSE_TOL = 1e-3
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import io_aware_amd
+    return io_aware_amd
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def compare(out, lse, ref_o, ref_l, dtype, label):
+    o = out.detach().float().cpu().numpy().astype(np.float64).reshape(ref_o.shape)
+    l = lse.detach().float().cpu().numpy().astype(np.float64).reshape(ref_l.shape)
+    assert np.isfinite(o).all(), label + ": non-finite O"
+    assert np.isfinite(l).all(), label + ": non-finite LSE"
+    err = np.abs(o - ref_o)
+    lerr = np.abs(l - ref_l)
+    max_tol, mean_tol = TOL[dtype]
+    note("%s: max|dO|=%.3e mean|dO|=%.3e max|dLSE|=%.3e" % (label, err.max(), err.mean(), lerr.max()))
+    assert err.max() <= max_tol, "%s: max|dO| %.3e > %.1e" % (label, err.max(), max_tol)
+    if mean_tol is not None:
+        assert err.mean() <= mean_tol, "%s: mean|dO| %.3e > %.1e" % (label, err.mean(), mean_tol)
+    assert lerr.max() <= LSE_TOL, "%s: max|dLSE| %.3e > %.1e" % (label, lerr.max(), LSE_TOL)
+
+
+def to_dev(*ts):
+    return [t.to(DEV).contiguous() for t in ts]
+
+
+def run_full(fa, B, H, Nq, Nk, d, dtype, causal, seed, q_sigma=1.0, label=None):
+    label = label or "B%d H%d Nq%d Nk%d d%d %s causal=%d" % (B, H, Nq, Nk, d, dtype, causal)
+    note("case " + label)
+    q, k, v = fa_inputs.make_qkv(B, H, Nq, Nk, d, dtype, seed, q_sigma)
+    scale = fa_inputs.default_scale(d)
+    qd, kd, vd = to_dev(q, k, v)
+    out, lse = fa.fa_fwd(qd, kd, vd, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.attention(q, k, v, scale, causal)
+    compare(out, lse, ref_o, ref_l, dtype, label)
+    return q, k, v, out, lse
+
+
+# ---------------------------------------------------------------------------
+# The five workloads
+# ---------------------------------------------------------------------------
+
+def test_single_head_f32(fa):
+    w = fa_inputs.WORKLOADS["single_head_f32_n256_d64"]
+    run_full(fa, w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.causal, w.seed, label=w.name)
+
+
+def test_ragged_causal_f16(fa):
+    w = fa_inputs.WORKLOADS["ragged_causal_f16_b2h8_n1000_d64"]
+    run_full(fa, w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.causal, w.seed, label=w.name)
+
+
+@pytest.mark.parametrize("name,nrows", [("prefill_causal_bf16_b8h16_n4096_d128", 3000),
+                                        ("long_bf16_b1h32_n16384_d128_qsigma8", 1500)])
+def test_full_size_prefill_sampled_rows(fa, name, nrows):
+    w = fa_inputs.WORKLOADS[name]
+    note("case %s (sampled %d rows)" % (name, nrows))
+    q, k, v = fa_inputs.make_workload(w)
+    qd, kd, vd = to_dev(q, k, v)
+    out, lse = fa.fa_fwd(qd, kd, vd, scale=w.scale, causal=w.causal)
+    torch.cuda.synchronize()
+    rows = fa_inputs.sample_rows(w.B, w.H, w.Nq, nrows, seed=w.seed)
+    ref_o, ref_l = oracle.attention(q, k, v, w.scale, w.causal, rows=rows)
+    o = out.reshape(-1, w.d)[torch.from_numpy(rows).to(DEV)]
+    l = lse.reshape(-1)[torch.from_numpy(rows).to(DEV)]
+    compare(o, l, ref_o, ref_l, w.dtype, name)
+    # every output row is finite, not only the sampled ones
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+
+
+def test_decode_split32_full(fa):
+    w = fa_inputs.WORKLOADS["decode_bf16_b16h32_nk8192_d128_split32"]
+    note("case " + w.name)
+    q, k, v = fa_inputs.make_workload(w)
+    qd, kd, vd = to_dev(q, k, v)
+    ref_o, ref_l = oracle.attention(q, k, v, w.scale, False)
+    out, lse = fa.fa_fwd_splitkv(qd, kd, vd, w.num_splits, scale=w.scale)
+    torch.cuda.synchronize()
+    compare(out, lse, ref_o, ref_l, w.dtype, w.name + " (fa_fwd_splitkv)")
+    out2, lse2 = fa.fa_fwd(qd, kd, vd, scale=w.scale)   # default splits: 32 for 8192 keys
+    torch.cuda.synchronize()
+    assert fa.fa_default_num_splits(w.Nk) == w.num_splits
+    assert torch.equal(out2, out) and torch.equal(lse2, lse)
+
+
+# ---------------------------------------------------------------------------
+# Ragged shapes spanning several tiles, every head dim and type
+# ---------------------------------------------------------------------------
+
+SHAPES = [(1, 2, 300, 517), (2, 1, 517, 300), (1, 1, 129, 64), (1, 3, 64, 1), (1, 1, 1, 77),
+          (1, 2, 255, 255), (1, 1, 513, 513)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_shapes(fa, dtype, d, causal):
+    for i, (B, H, Nq, Nk) in enumerate(SHAPES):
+        run_full(fa, B, H, Nq, Nk, d, dtype, causal, seed=100 + i + 10 * d)
+
+
+@pytest.mark.parametrize("shape_id", [0, 1, 2])
+def test_every_prefill_tile_shape(fa, shape_id, monkeypatch):
+    monkeypatch.setenv("FA_PREFILL_SHAPE", str(shape_id))
+    for d in (64, 128):
+        for causal in (False, True):
+            run_full(fa, 1, 2, 700, 700, d, "bf16", causal, seed=7 + d, q_sigma=4.0,
+                     label="shape %d d%d causal=%d" % (shape_id, d, causal))
+
+
+def test_triton_page_regression(fa):
+    """The fp16 shapes and seed of the Triton page's test; its bound is
+    max-abs < 1e-3 against an fp16 torch reference, here against fp64."""
+    import json
+    spec = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "triton_page_test.json")))
+    for (Nq, Nk, d) in spec["shapes_nq_nk_d"]:
+        q, k, v = fa_inputs.make_qkv(1, 1, Nq, Nk, d, "f16", spec["seed"])
+        scale = fa_inputs.default_scale(d)
+        out, lse = fa.fa_fwd(*to_dev(q, k, v), scale=scale)
+        torch.cuda.synchronize()
+        ref_o, _ = oracle.attention(q, k, v, scale, False)
+        err = np.abs(out.float().cpu().numpy() - ref_o).max()
+        note("triton page case %dx%dx%d: max|dO| = %.3e" % (Nq, Nk, d, err))
+        assert err < spec["max_abs_tol"]
+
+
+# ---------------------------------------------------------------------------
+# Split-KV edge cases
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("Nk,S", [(8192, 1), (1000, 7), (50, 64), (1, 1), (513, 32), (4096, 1024)])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_splitkv_edge_cases(fa, Nk, S, dtype):
+    note("case splitkv Nk=%d S=%d %s" % (Nk, S, dtype))
+    q, k, v = fa_inputs.make_qkv(2, 3, 1, Nk, 128, dtype, seed=Nk + S, q_sigma=3.0)
+    scale = fa_inputs.default_scale(128)
+    out, lse = fa.fa_fwd_splitkv(*to_dev(q, k, v), S, scale=scale)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.attention(q, k, v, scale, False)
+    compare(out, lse, ref_o, ref_l, dtype, "splitkv Nk=%d S=%d" % (Nk, S))
+
+
+# ---------------------------------------------------------------------------
+# Invariants, determinism, guard bands
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_constant_values_give_that_constant(fa, dtype):
+    q, k, v = fa_inputs.make_qkv(1, 2, 333, 333, 128, dtype, seed=21, q_sigma=8.0)
+    v[:] = v[:, :, :1, :]                       # every value row equal
+    for causal in (False, True):
+        out, _ = fa.fa_fwd(*to_dev(q, k, v), causal=causal)
+        torch.cuda.synchronize()
+        c = v[:, :, :1, :].float().expand_as(out).cpu()
+        rel = ((out.float().cpu() - c).abs() / c.abs().clamp_min(1e-3)).max().item()
+        assert rel <= 2.0 ** -7, rel        # within one unit in the last place of the 16-bit type
+
+
+def test_causal_first_row_and_single_query(fa):
+    q, k, v = fa_inputs.make_qkv(2, 2, 200, 200, 64, "bf16", seed=22, q_sigma=8.0)
+    out, lse = fa.fa_fwd(*to_dev(q, k, v), causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out[:, :, 0].cpu(), v[:, :, 0])       # only key 0 is visible: P = 1 exactly
+    q1 = q[:, :, :1].contiguous()
+    out1, _ = fa.fa_fwd(*to_dev(q1, k, v), causal=True)      # Nq = 1 under the mask: key 0 only
+    torch.cuda.synchronize()
+    assert torch.equal(out1[:, :, 0].cpu(), v[:, :, 0])
+
+
+def test_key_value_permutation_equivariance(fa):
+    q, k, v = fa_inputs.make_qkv(1, 2, 256, 300, 128, "bf16", seed=23)
+    perm = torch.from_numpy(np.random.default_rng(0).permutation(300))
+    o1, l1 = fa.fa_fwd(*to_dev(q, k, v))
+    o2, l2 = fa.fa_fwd(*to_dev(q, k[:, :, perm].contiguous(), v[:, :, perm].contiguous()))
+    torch.cuda.synchronize()
+    assert (o1.float() - o2.float()).abs().max().item() <= 2e-2
+    assert (l1 - l2).abs().max().item() <= 1e-3
+
+
+def test_bitwise_deterministic(fa):
+    q, k, v = fa_inputs.make_qkv(2, 4, 1000, 1000, 128, "bf16", seed=24)
+    qd, kd, vd = to_dev(q, k, v)
+    for causal in (False, True):
+        a = fa.fa_fwd(qd, kd, vd, causal=causal)
+        b = fa.fa_fwd(qd, kd, vd, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("dtype,Nq,Nk,causal", [("bf16", 1000, 1000, True), ("f32", 100, 70, False),
+                                                ("bf16", 1, 8192, False), ("f16", 77, 33, True)])
+def test_guard_bands_untouched(fa, dtype, Nq, Nk, causal):
+    B, H, d = 2, 3, 128
+    q, k, v = fa_inputs.make_qkv(B, H, Nq, Nk, d, dtype, seed=25)
+    qd, kd, vd = to_dev(q, k, v)
+    n_out, n_lse, pad = B * H * Nq * d, B * H * Nq, 4096
+    tdt = fa_inputs.DTYPES[dtype]
+    obuf = torch.full((n_out + 2 * pad,), 7.0, dtype=tdt, device=DEV)
+    lbuf = torch.full((n_lse + 2 * pad,), 7.0, dtype=torch.float32, device=DEV)
+    out = obuf[pad:pad + n_out].view(B, H, Nq, d)
+    lse = lbuf[pad:pad + n_lse].view(B, H, Nq)
+    fa.fa_fwd(qd, kd, vd, causal=causal, out=out, lse=lse)
+    torch.cuda.synchronize()
+    for buf, n in ((obuf, n_out), (lbuf, n_lse)):
+        assert (buf[:pad].float() == 7.0).all() and (buf[pad + n:].float() == 7.0).all()
+    ref_o, ref_l = oracle.attention(q, k, v, fa_inputs.default_scale(d), causal)
+    compare(out, lse, ref_o, ref_l, dtype, "guard bands %s" % dtype)
+
+
+def test_lse_optional(fa):
+    q, k, v = fa_inputs.make_qkv(1, 2, 100, 100, 64, "bf16", seed=26)
+    qd, kd, vd = to_dev(q, k, v)
+    o1, _ = fa.fa_fwd(qd, kd, vd, return_lse=False)
+    o2, _ = fa.fa_fwd(qd, kd, vd)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
