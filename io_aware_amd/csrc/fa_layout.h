@@ -15,6 +15,21 @@
 // s = 0..7, with the same kslot function for A and B.  The contraction sums
 // over all 16 k, so any kslot assignment that A and B share gives the same
 // product; the kernel only relies on that.
+//
+// Staging.  K and V tiles ([BC keys][D dims] of 2-byte elements, row-major)
+// are copied from device memory into LDS by buffer-to-LDS DMA: one
+// instruction moves 16 bytes per lane and places lane t's 16 bytes at LDS
+// unit (base + t) -- the destination is fixed by the lane, so a layout is
+// chosen by picking which source chunk each lane fetches.  LDS unit
+// (key, pos) of a tile holds the key's 8-dim chunk pos ^ f(key); the XOR
+// swizzles f keep the operand reads free of bank conflicts.
+//
+// Transposed LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane j supplies an address of 4 consecutive 16-bit elements M[j][0..3];
+// lane i receives M[4e + i/4][i % 4] for e = 0..3.  Pointing lane j at
+// V[k0 + j/4][d0 + 4*(j % 4)] therefore gives lane i the column
+// V[k0 .. k0+3][d0 + i]: four consecutive keys of one head dim, which is what
+// the A operand of O^T = V^T P^T needs.
 #pragma once
 
 #if defined(__HIPCC__)
@@ -27,62 +42,84 @@ namespace fa {
 namespace layout {
 
 // ---------------------------------------------------------------------------
-// S^T accumulator: key (within the 32-key block) of register r in lane half g
+// Accumulator and P^T layouts
 // ---------------------------------------------------------------------------
+
+// Key (within a 32-key block) of S^T register r in lane half g.
 FA_HD int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
 
 // P^T as the B operand of O^T += V^T P^T: k-step ks2 covers keys
 // [16*ks2, 16*ks2 + 16) of the tile; slot s of lane half g holds the key that
 // S^T register r = 8*(ks2 % 2) + s of 32-key block ks2 / 2 holds.
-FA_HD int pv_key(int ks2, int g, int s) {
-    return 32 * (ks2 >> 1) + acc_row(8 * (ks2 & 1) + s, g);
-}
+FA_HD int pv_key(int ks2, int g, int s) { return 32 * (ks2 >> 1) + acc_row(8 * (ks2 & 1) + s, g); }
 
 // ---------------------------------------------------------------------------
-// K tile in LDS: row-major [BC keys][D dims] of 2-byte elements, 16-byte
-// chunks (8 dims) XOR-swizzled by the key so that the 32 lanes reading one
-// chunk column of 32 consecutive keys spread over all banks.
+// Swizzles: LDS unit (key, pos) holds 8-dim chunk pos ^ f(key)
 // ---------------------------------------------------------------------------
 template <int D>
-FA_HD int k_lds_offset(int key, int chunk) {
-    constexpr int CH = D / 8;  // 16-byte chunks per key row
-    return key * (D * 2) + ((chunk ^ (key & (CH - 1))) * 16);
+FA_HD int k_swizzle(int key) {   // spreads 8 consecutive keys of one chunk column
+    return key & 7 & (D / 8 - 1);
 }
 
-// A operand of S^T += K_blk Q^T for k-step ks (dims 16*ks .. 16*ks+15): lane
-// (row l32, half g) reads the 8 dims [16*ks + 8*g, 16*ks + 8*g + 8) of key
-// 32*kb + l32 as one 16-byte chunk.
+template <int D>
+FA_HD int v_swizzle(int key) {   // spreads the 4 keys x 2 chunks a transposed read touches
+    return (2 * (key & 3)) & (D / 8 - 1);
+}
+
+// Byte offset of element (key, dim) of a K or V tile in LDS.
+template <int D>
+FA_HD int k_elem_offset(int key, int dim) {
+    return key * (D * 2) + (((dim >> 3) ^ k_swizzle<D>(key)) << 4) + (dim & 7) * 2;
+}
+template <int D>
+FA_HD int v_elem_offset(int key, int dim) {
+    return key * (D * 2) + (((dim >> 3) ^ v_swizzle<D>(key)) << 4) + (dim & 7) * 2;
+}
+
+// DMA: LDS unit u of a tile (u = 64 * instruction_slot + lane) receives
+// source chunk (key, chunk) with key = u / (D/8), chunk = (u % (D/8)) ^ f(key).
+// Returned: element offset of that chunk within the tile's rows.
+template <int D>
+FA_HD int k_dma_src_elem(int u) {
+    constexpr int CH = D / 8;
+    const int key = u / CH;
+    return key * D + (((u % CH) ^ k_swizzle<D>(key)) * 8);
+}
+template <int D>
+FA_HD int v_dma_src_elem(int u) {
+    constexpr int CH = D / 8;
+    const int key = u / CH;
+    return key * D + (((u % CH) ^ v_swizzle<D>(key)) * 8);
+}
+
+// ---------------------------------------------------------------------------
+// Operand reads
+// ---------------------------------------------------------------------------
+
+// A operand of S^T += K_blk Q^T, k-step ks (dims 16*ks .. 16*ks+15): lane
+// (row l32, half g) reads dims [16*ks + 8*g, +8) of key 32*kb + l32 as one
+// 16-byte chunk.
 template <int D>
 FA_HD int k_operand_offset(int kb, int l32, int g, int ks) {
-    return k_lds_offset<D>(32 * kb + l32, 2 * ks + g);
+    return k_elem_offset<D>(32 * kb + l32, 16 * ks + 8 * g);
 }
 
-// ---------------------------------------------------------------------------
-// V tile in LDS, transposed: [D dims][BC keys] of 2-byte elements.  Each dim
-// row is cut into 8-byte slots of 4 consecutive keys.  Within every 16 keys
-// the slots are ordered (keys 0-3, 8-11, 4-7, 12-15) so that the 8 keys one
-// lane half needs for a P^T k-step sit in two adjacent slots; the slot index
-// is XOR-swizzled by f(dim) = dim ^ (dim >> 3) so that both the writers
-// (8 dims apart) and the readers (consecutive dims) avoid bank conflicts.
-// ---------------------------------------------------------------------------
-FA_HD int vt_slot_of_group(int u) {           // u: 4-key group, keys 4u..4u+3
-    const int u4 = u & 3;
-    return 4 * (u >> 2) + (((u4 & 1) << 1) | (u4 >> 1));
+// A operand of O^T += V^T P^T for dim block db, k-step ks2 and slot half sh
+// (slots 4*sh .. 4*sh+3 = keys 16*ks2 + 8*sh + 4*g + 0..3): the address lane
+// (group G = lane / 16, j = lane % 16) hands to the transposed read.  Lane
+// half g = G / 2; dims 32*db + 16*(G % 2) + [0, 16) are the group's columns.
+template <int D>
+FA_HD int v_operand_tr_offset(int db, int lane, int ks2, int sh) {
+    const int G = lane >> 4, j = lane & 15;
+    const int key = 16 * ks2 + 8 * sh + 4 * (G >> 1) + (j >> 2);
+    const int dim = 32 * db + 16 * (G & 1) + 4 * (j & 3);
+    return v_elem_offset<D>(key, dim);
 }
 
-template <int BC>
-FA_HD int vt_lds_offset(int dim, int slot) {
-    constexpr int NSLOT = BC / 4;
-    return dim * (BC * 2) + ((slot ^ ((dim ^ (dim >> 3)) & (NSLOT - 1))) * 8);
-}
-
-// A operand of O^T += V^T P^T for dim block db and k-step ks2: lane
-// (dim 32*db + l32, half g) reads slot 4*ks2 + 2*g (keys 16*ks2 + 4g + 0..3)
-// and slot 4*ks2 + 2*g + 1 (keys 16*ks2 + 8 + 4g + 0..3).
-template <int BC>
-FA_HD int v_operand_offset(int db, int l32, int g, int ks2, int half) {
-    return vt_lds_offset<BC>(32 * db + l32, 4 * ks2 + 2 * g + half);
-}
+// Model of the transposed read for host checks: the (address owner lane,
+// element) that lane i's element e comes from, within its 16-lane group.
+FA_HD int tr_src_lane(int i, int e) { return 4 * e + (i >> 2); }
+FA_HD int tr_src_elem(int i) { return i & 3; }
 
 // ---------------------------------------------------------------------------
 // Workgroup order.  Workgroup wg of nwg = BH * Tr goes to XCD wg % 8 in

@@ -11,20 +11,24 @@
 // after the last block O = acc / l and LSE = m + ln l.  Score and
 // probability tiles live only in registers.
 //
-// CDNA4 design:
+// CDNA4 design (index arithmetic in fa_layout.h, checked on the host):
 //  * 32x32x16 bf16/fp16 MFMA in transposed orientation: S^T = K Q^T and
 //    O^T = V^T P^T.  Each lane's 16 accumulator registers of a 32x32 block
 //    belong to one query, so the row max is 16 in-register maxima plus one
-//    exchange between lane halves, the rescale factor is a per-lane scalar,
-//    and the S^T registers convert in place into the P^T operand of the
-//    second product (no LDS round trip for P).
+//    exchange between lane halves (v_permlane32_swap), the rescale factor is
+//    a per-lane scalar, and the S^T registers convert in place into the P^T
+//    operand of the second product (no LDS round trip for P).
 //  * Q fragments are loaded once into registers and stay there.
-//  * K is staged row-major, V transposed (key-contiguous per head dim), in
-//    LDS with XOR swizzles chosen so that the staging writes and the operand
-//    reads are free of bank conflicts (layout arithmetic in fa_layout.h).
-//  * Two LDS stages: the global loads of block j+1 are issued before block j
-//    is computed and written to the other stage afterwards (one barrier per
-//    block).
+//  * K and V tiles go from device memory straight into LDS by buffer-to-LDS
+//    DMA (no staging registers, no staging ALU work; the tile's key offset
+//    is a scalar), row-major with XOR swizzles.  The V^T operand is gathered
+//    by the gfx950 transposing LDS read, four keys of one head dim per lane.
+//  * Two LDS stages: the DMA of block j+1 is issued before block j is
+//    computed (one barrier per block).  The block loop is unrolled by two so
+//    that stage offsets, like the block and k-step offsets, fold into
+//    instruction immediates; per-lane address parts are computed once.
+//  * Registers are budgeted for two waves per SIMD: a CU holds two
+//    independent workgroups whose MFMA and softmax phases overlap.
 //  * exp is computed as exp2 with scale*log2(e) folded into one FMA.
 //  * Lazy rescale: the accumulator is rescaled only when some row's max has
 //    grown by more than 2^8 (in the exp2 domain) over the max it is held
@@ -35,12 +39,16 @@
 //  * Causal: K/V blocks after a workgroup's last query are never loaded;
 //    a wave skips the MFMA work of blocks entirely after its own last query;
 //    only blocks that cross the diagonal or the ragged key tail are masked.
+//    Rows of the ragged key tail are fetched from the last key (finite data
+//    that the mask removes), so no load leaves the tensor.
 //  * Workgroup order: whole heads per XCD, longest causal blocks first.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "fa_internal.h"
 #include "fa_layout.h"
+
+#define FA_LDS __attribute__((address_space(3)))
 
 namespace fa {
 namespace {
@@ -53,7 +61,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 template <typename T>
 struct Mfma;
@@ -76,6 +85,11 @@ struct Mfma<_Float16> {
     }
 };
 
+template <int N>
+struct Int {
+    static constexpr int value = N;
+};
+
 struct PrefillArgs {
     const void *q;
     const void *k;
@@ -92,9 +106,22 @@ struct PrefillArgs {
 // Held-max slack in the exp2 domain: P is at most 2^8 between rescales.
 constexpr float kRescaleSlack = 8.0f;
 constexpr float kLn2 = 0.693147180559945309417f;
+// word 3 of a raw buffer descriptor on gfx9-family parts
+constexpr int kBufferDword3 = 0x00020000;
 
-template <typename T, int D, bool CAUSAL, int NW, int QW, int BC>
-__global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
+__device__ __forceinline__ float xor32_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float xor32_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <typename T, int D, bool CAUSAL, int NW, int QW, int BC, int OCC>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC)))
+void prefill_kernel(PrefillArgs a) {
     using M = Mfma<T>;
     using x8 = typename M::x8;
     using x4 = typename M::x4;
@@ -106,20 +133,20 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     constexpr int KB = BC / 32;      // 32-key row blocks of S^T
     constexpr int KS2 = BC / 16;     // k-steps of O^T = V^T P^T
     constexpr int CH = D / 8;        // 16-byte chunks per row of K or V
-    constexpr int TILE_BYTES = BC * D * 2;
-    constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K tile + V^T tile
-    constexpr int K_CHUNKS = BC * CH;            // staging items of a K tile
-    constexpr int NKL = (K_CHUNKS + NT - 1) / NT;
-    constexpr int V_ITEMS = (BC / 4) * CH;       // (4-key group, dim chunk) items
-    constexpr int NVL = (V_ITEMS + NT - 1) / NT;
+    constexpr int ROW = D * 2;       // bytes per key row
+    constexpr int TILE_BYTES = BC * ROW;
+    constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K tile + V tile
+    constexpr int UNITS = BC * CH;               // 16-byte units per tile
+    constexpr int NDMA = UNITS / NT;             // DMA instructions per thread per tile (each of K, V)
     static_assert(QW % 32 == 0 && BC % 32 == 0 && D % 32 == 0, "tile shape");
-    static_assert(BC / 4 <= 32, "V^T slot swizzle covers at most 32 slots");
+    static_assert(UNITS % NT == 0, "a tile must split evenly over the workgroup");
+    static_assert(2 * STAGE_BYTES <= 65536, "stage offsets must fit a 16-bit LDS immediate");
 
-    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31;
     const int g = lane >> 5;
 
@@ -133,6 +160,47 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     const T *kp = static_cast<const T *>(a.k) + (size_t)bh * Nk * D;
     const T *vp = static_cast<const T *>(a.v) + (size_t)bh * Nk * D;
     const float c = a.scale_log2;
+    const uint32_t kv_bytes = (uint32_t)Nk * ROW;
+    const __amdgpu_buffer_rsrc_t rsrc_k = __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(kp), (short)0, (int)kv_bytes, kBufferDword3);
+    const __amdgpu_buffer_rsrc_t rsrc_v = __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(vp), (short)0, (int)kv_bytes, kBufferDword3);
+
+    // per-lane DMA source offsets (bytes, relative to the tile's first key)
+    uint32_t kdma[NDMA], vdma[NDMA];
+    int dkey[NDMA];
+#pragma unroll
+    for (int n = 0; n < NDMA; ++n) {
+        const int u = (n * NW + wave) * 64 + lane;
+        kdma[n] = (uint32_t)layout::k_dma_src_elem<D>(u) * 2;
+        vdma[n] = (uint32_t)layout::v_dma_src_elem<D>(u) * 2;
+        dkey[n] = u / CH;
+    }
+    // per-lane operand read offsets (bytes within a tile, block / k-step 0)
+    int koff[KS], voff[DB];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) koff[ks] = layout::k_operand_offset<D>(0, l32, g, ks);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) voff[db] = layout::v_operand_tr_offset<D>(db, lane, 0, 0);
+
+    auto issue_tile = [&](int k0, int stage) {
+        char *kbase = smem + stage * STAGE_BYTES;
+        char *vbase = kbase + TILE_BYTES;
+        const uint32_t soff = (uint32_t)k0 * ROW;
+        const bool tail = k0 + BC > Nk;  // workgroup-uniform
+#pragma unroll
+        for (int n = 0; n < NDMA; ++n) {
+            uint32_t ko = kdma[n], vo = vdma[n];
+            if (tail) {
+                const int over = k0 + dkey[n] - (Nk - 1);  // rows past the end: fetch the last key instead
+                if (over > 0) {
+                    ko -= (uint32_t)over * ROW;
+                    vo -= (uint32_t)over * ROW;
+                }
+            }
+            const int dst = (n * NW + wave) * 1024;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_k, (FA_LDS void *)(kbase + dst), 16, ko, soff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_v, (FA_LDS void *)(vbase + dst), 16, vo, soff, 0, 0);
+        }
+    };
 
     // Q fragments (B operand of S^T): lane (query l32 of block qb, half g)
     // holds dims [16*ks + 8*g, +8).
@@ -143,8 +211,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             u32x4 raw = {0u, 0u, 0u, 0u};
-            if (row < Nq)
-                raw = *reinterpret_cast<const u32x4 *>(qp + (size_t)row * D + 16 * ks + 8 * g);
+            if (row < Nq) raw = *reinterpret_cast<const u32x4 *>(qp + (size_t)row * D + 16 * ks + 8 * g);
             qf[qb][ks] = __builtin_bit_cast(x8, raw);
         }
     }
@@ -165,198 +232,130 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     const int kv_end = CAUSAL ? min(Nk, q0 + BR) : Nk;
     const int nt = (kv_end + BC - 1) / BC;
 
-    u32x4 kst[NKL];
-    u32x4 vst[NVL][4];
-
-    auto load_tile = [&](int k0) {
+    auto compute_tile = [&](auto stage_tag, int k0) {
+        constexpr int S = decltype(stage_tag)::value;
+        constexpr int KOFF = S * STAGE_BYTES;
+        constexpr int VOFF = KOFF + TILE_BYTES;
+        // ---- S^T = K_blk Q^T -------------------------------------------------
+        f32x16 s[QB][KB];
 #pragma unroll
-        for (int i = 0; i < NKL; ++i) {
-            const int item = tid + i * NT;
-            kst[i] = u32x4{0u, 0u, 0u, 0u};
-            if ((K_CHUNKS % NT) == 0 || item < K_CHUNKS) {
-                const int key = k0 + item / CH;
-                const int ch = item % CH;
-                if (key < Nk)
-                    kst[i] = *reinterpret_cast<const u32x4 *>(kp + (size_t)key * D + ch * 8);
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const x8 kf = __builtin_bit_cast(
+                    x8, *reinterpret_cast<const u32x4 *>(smem + KOFF + kb * 32 * ROW + koff[ks]));
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) s[qb][kb] = M::run(kf, qf[qb][ks], s[qb][kb]);
             }
         }
-#pragma unroll
-        for (int i = 0; i < NVL; ++i) {
-            const int item = tid + i * NT;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) vst[i][j] = u32x4{0u, 0u, 0u, 0u};
-            if ((V_ITEMS % NT) == 0 || item < V_ITEMS) {
-                const int u = item / CH;
-                const int dc = item % CH;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int key = k0 + 4 * u + j;
-                    if (key < Nk)
-                        vst[i][j] = *reinterpret_cast<const u32x4 *>(vp + (size_t)key * D + dc * 8);
-                }
-            }
-        }
-    };
 
-    auto store_tile = [&](int buf) {
-        char *ks_lds = smem + buf * STAGE_BYTES;
-        char *vs_lds = ks_lds + TILE_BYTES;
-#pragma unroll
-        for (int i = 0; i < NKL; ++i) {
-            const int item = tid + i * NT;
-            if ((K_CHUNKS % NT) == 0 || item < K_CHUNKS) {
-                const int key = item / CH;
-                const int ch = item % CH;
-                *reinterpret_cast<u32x4 *>(ks_lds + layout::k_lds_offset<D>(key, ch)) = kst[i];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < NVL; ++i) {
-            const int item = tid + i * NT;
-            if ((V_ITEMS % NT) == 0 || item < V_ITEMS) {
-                const int u = item / CH;
-                const int dc = item % CH;
-                const int slot = layout::vt_slot_of_group(u);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    // head dim 8*dc + e of keys 4u .. 4u+3, packed two per dword
-                    const int w = e >> 1;
-                    uint32_t lo, hi;
-                    if (e & 1) {
-                        lo = (vst[i][0][w] >> 16) | (vst[i][1][w] & 0xffff0000u);
-                        hi = (vst[i][2][w] >> 16) | (vst[i][3][w] & 0xffff0000u);
-                    } else {
-                        lo = (vst[i][0][w] & 0xffffu) | (vst[i][1][w] << 16);
-                        hi = (vst[i][2][w] & 0xffffu) | (vst[i][3][w] << 16);
-                    }
-                    *reinterpret_cast<u32x2 *>(vs_lds + layout::vt_lds_offset<BC>(8 * dc + e, slot)) =
-                        u32x2{lo, hi};
-                }
-            }
-        }
-    };
-
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-
-    for (int jt = 0; jt < nt; ++jt) {
-        const int k0 = jt * BC;
-        const bool has_next = jt + 1 < nt;
-        if (has_next) load_tile(k0 + BC);
-
-        const char *ks_lds = smem + (jt & 1) * STAGE_BYTES;
-        const char *vs_lds = ks_lds + TILE_BYTES;
-        // wave-uniform: the wave has live queries that see some key of this block
-        const bool active = (q0w < Nq) && (!CAUSAL || k0 <= q0w + QW - 1);
-        if (active) {
-            // ---- S^T = K_blk Q^T -------------------------------------------
-            f32x16 s[QB][KB];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.0f;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const x8 kf = __builtin_bit_cast(
-                        x8, *reinterpret_cast<const u32x4 *>(
-                                ks_lds + layout::k_operand_offset<D>(kb, l32, g, ks)));
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) s[qb][kb] = M::run(kf, qf[qb][ks], s[qb][kb]);
-                }
-            }
-
-            // ---- mask: ragged key tail and the causal diagonal --------------
-            const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > q0w);
-            if (need_mask) {
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    const int qrow = q0w + 32 * qb + l32;
-#pragma unroll
-                    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int key = k0 + 32 * kb + layout::acc_row(r, g);
-                            if (key >= Nk || (CAUSAL && key > qrow)) s[qb][kb][r] = -__builtin_inff();
-                        }
-                }
-            }
-
-            // ---- online softmax ---------------------------------------------
+        // ---- mask: ragged key tail and the causal diagonal ------------------
+        const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > q0w);
+        if (need_mask) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
-                float mx = -__builtin_inff();
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[qb][kb][r]);
-                mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
-                const float mt = mx * c;  // block max in the exp2 domain (c > 0)
-                if (__ballot(mt > m_held[qb] + kRescaleSlack) != 0ull) {
-                    const float m_new = __builtin_fmaxf(m_held[qb], mt);
-                    const float alpha =
-                        (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_held[qb] - m_new);
-                    m_held[qb] = m_new;
-                    l_part[qb] *= alpha;
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha;
-                }
-                // a row that has seen no key yet keeps m = -inf: subtract 0
-                // there so masked scores give exp2(-inf) = 0, not NaN
-                const float msub = (m_held[qb] == -__builtin_inff()) ? 0.0f : m_held[qb];
-                float lsum = 0.0f;
+                const int qrow = q0w + 32 * qb + l32;
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][r], c, -msub));
-                        s[qb][kb][r] = p;
-                        lsum += p;
+                        const int key = k0 + 32 * kb + layout::acc_row(r, g);
+                        if (key >= Nk || (CAUSAL && key > qrow)) s[qb][kb][r] = -__builtin_inff();
                     }
-                l_part[qb] += lsum;
-            }
-
-            // ---- O^T += V^T P^T ---------------------------------------------
-            x8 pf[QB][KS2];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                for (int ks2 = 0; ks2 < KS2; ++ks2) {
-                    const int kb = ks2 >> 1;
-                    const int h = (ks2 & 1) * 8;
-                    f32x8 t;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) t[e] = s[qb][kb][h + e];
-                    pf[qb][ks2] = __builtin_convertvector(t, x8);
-                }
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-#pragma unroll
-                for (int ks2 = 0; ks2 < KS2; ++ks2) {
-                    const u32x2 lo = *reinterpret_cast<const u32x2 *>(
-                        vs_lds + layout::v_operand_offset<BC>(db, l32, g, ks2, 0));
-                    const u32x2 hi = *reinterpret_cast<const u32x2 *>(
-                        vs_lds + layout::v_operand_offset<BC>(db, l32, g, ks2, 1));
-                    const x8 vf = __builtin_bit_cast(x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = M::run(vf, pf[qb][ks2], oacc[qb][db]);
-                }
             }
         }
 
-        if (has_next) store_tile((jt + 1) & 1);
-        __syncthreads();
+        // ---- online softmax -------------------------------------------------
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            float mx = -__builtin_inff();
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[qb][kb][r]);
+            mx = xor32_max(mx);
+            const float mt = mx * c;  // block max in the exp2 domain (c > 0)
+            if (__ballot(mt > m_held[qb] + kRescaleSlack) != 0ull) {
+                const float m_new = __builtin_fmaxf(m_held[qb], mt);
+                const float alpha =
+                    (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_held[qb] - m_new);
+                m_held[qb] = m_new;
+                l_part[qb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha;
+            }
+            // a row that has seen no key yet keeps m = -inf: subtract 0 there
+            // so masked scores give exp2(-inf) = 0, not NaN
+            const float msub = (m_held[qb] == -__builtin_inff()) ? 0.0f : m_held[qb];
+            float lsum = 0.0f;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][r], c, -msub));
+                    s[qb][kb][r] = p;
+                    lsum += p;
+                }
+            l_part[qb] += lsum;
+        }
+
+        // ---- O^T += V^T P^T -------------------------------------------------
+        x8 pf[QB][KS2];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int ks2 = 0; ks2 < KS2; ++ks2) {
+                const int kb = ks2 >> 1;
+                const int h = (ks2 & 1) * 8;
+                f32x8 t;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) t[e] = s[qb][kb][h + e];
+                pf[qb][ks2] = __builtin_convertvector(t, x8);
+            }
+#pragma unroll
+        for (int ks2 = 0; ks2 < KS2; ++ks2) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const char *base = smem + VOFF + voff[db] + 16 * ks2 * ROW;
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4 *)(base));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4 *)(base + 8 * ROW));
+                const x8 vf = __builtin_bit_cast(x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = M::run(vf, pf[qb][ks2], oacc[qb][db]);
+            }
+        }
+    };
+
+    auto step = [&](auto stage_tag, int jt) {
+        constexpr int S = decltype(stage_tag)::value;
+        const int k0 = jt * BC;
+        if (jt + 1 < nt) issue_tile(k0 + BC, S ^ 1);
+        // wave-uniform: the wave has live queries that see some key of this block
+        const bool active = (q0w < Nq) && (!CAUSAL || k0 <= q0w + QW - 1);
+        if (active) compute_tile(stage_tag, k0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's DMA of block jt+1 has landed
+        __syncthreads();                                    // ... and every thread's; stage S is free
+    };
+
+    issue_tile(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int jt = 0; jt < nt; jt += 2) {
+        step(Int<0>{}, jt);
+        if (jt + 1 < nt) step(Int<1>{}, jt + 1);
     }
 
     // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2 --------------------
     T *op = static_cast<T *>(a.out) + (size_t)bh * Nq * D;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        const float l = l_part[qb] + __shfl_xor(l_part[qb], 32);
+        const float l = xor32_sum(l_part[qb]);
         const int row = q0w + 32 * qb + l32;
         if (row < Nq) {
             const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
@@ -377,15 +376,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     }
 }
 
-template <int NW, int QW>
-struct ShapeOf {
-    static constexpr int kWaves = NW;
-    static constexpr int kQw = QW;
-};
-
-template <typename T, int D, bool CAUSAL, int NW, int QW>
-hipError_t launch_one(const void *q, const void *k, const void *v, void *out, float *lse,
-                      int BH, int Nq, int Nk, float scale_log2, hipStream_t stream) {
+template <typename T, int D, bool CAUSAL, int NW, int QW, int OCC>
+hipError_t launch_one(const void *q, const void *k, const void *v, void *out, float *lse, int BH, int Nq, int Nk,
+                      float scale_log2, hipStream_t stream) {
     constexpr int BC = 64;
     constexpr int BR = NW * QW;
     PrefillArgs a;
@@ -401,25 +394,25 @@ hipError_t launch_one(const void *q, const void *k, const void *v, void *out, fl
     a.scale_log2 = scale_log2;
     const long long nwg = (long long)BH * a.Tr;
     if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((prefill_kernel<T, D, CAUSAL, NW, QW, BC>), dim3((unsigned)nwg), dim3(NW * 64), 0,
+    hipLaunchKernelGGL((prefill_kernel<T, D, CAUSAL, NW, QW, BC, OCC>), dim3((unsigned)nwg), dim3(NW * 64), 0,
                        stream, a);
     return hipGetLastError();
 }
 
 template <typename T, int D, bool CAUSAL>
-hipError_t launch_shape(int shape, const void *q, const void *k, const void *v, void *out, float *lse,
-                        int BH, int Nq, int Nk, float sl, hipStream_t stream) {
+hipError_t launch_shape(int shape, const void *q, const void *k, const void *v, void *out, float *lse, int BH,
+                        int Nq, int Nk, float sl, hipStream_t stream) {
     switch (shape) {
-        case kShapeW4Q32: return launch_one<T, D, CAUSAL, 4, 32>(q, k, v, out, lse, BH, Nq, Nk, sl, stream);
-        case kShapeW4Q64: return launch_one<T, D, CAUSAL, 4, 64>(q, k, v, out, lse, BH, Nq, Nk, sl, stream);
-        case kShapeW2Q64: return launch_one<T, D, CAUSAL, 2, 64>(q, k, v, out, lse, BH, Nq, Nk, sl, stream);
+        case kShapeW4Q32: return launch_one<T, D, CAUSAL, 4, 32, 2>(q, k, v, out, lse, BH, Nq, Nk, sl, stream);
+        case kShapeW4Q64: return launch_one<T, D, CAUSAL, 4, 64, 1>(q, k, v, out, lse, BH, Nq, Nk, sl, stream);
+        case kShapeW2Q64: return launch_one<T, D, CAUSAL, 2, 64, 1>(q, k, v, out, lse, BH, Nq, Nk, sl, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <typename T>
-hipError_t launch_typed(int d, bool causal, int shape, const void *q, const void *k, const void *v,
-                        void *out, float *lse, int BH, int Nq, int Nk, float sl, hipStream_t stream) {
+hipError_t launch_typed(int d, bool causal, int shape, const void *q, const void *k, const void *v, void *out,
+                        float *lse, int BH, int Nq, int Nk, float sl, hipStream_t stream) {
 #define FA_CASE(DD)                                                                                  \
     case DD:                                                                                         \
         return causal ? launch_shape<T, DD, true>(shape, q, k, v, out, lse, BH, Nq, Nk, sl, stream)  \
@@ -444,9 +437,8 @@ int prefill_block_rows(int shape) {
     }
 }
 
-hipError_t launch_prefill(int dtype, int d, bool causal, int shape, const void *q, const void *k,
-                          const void *v, void *out, float *lse, int BH, int Nq, int Nk, float scale_log2,
-                          hipStream_t stream) {
+hipError_t launch_prefill(int dtype, int d, bool causal, int shape, const void *q, const void *k, const void *v,
+                          void *out, float *lse, int BH, int Nq, int Nk, float scale_log2, hipStream_t stream) {
     if (dtype == 2)
         return launch_typed<__bf16>(d, causal, shape, q, k, v, out, lse, BH, Nq, Nk, scale_log2, stream);
     if (dtype == 1)

@@ -2,14 +2,17 @@
 // (io_aware_amd/csrc/fa_layout.h), built with g++ by tests/test_layout.py.
 //
 // For each tile shape it proves, by enumeration, that
-//  * the K-tile staging writes cover the LDS tile exactly once, in range;
-//  * every S^T = K Q^T operand read returns the K element the MFMA lane
+//  * the DMA staging of a K or V tile places every source element exactly
+//    once, inside the tile, and where k_elem_offset / v_elem_offset say;
+//  * every S^T = K Q^T operand read returns the K elements the MFMA lane
 //    contract needs (key 32*kb + l32, dims 16*ks + 8*g .. +7);
-//  * the transposed V staging writes cover the V^T tile exactly once;
-//  * every O^T = V^T P^T operand read returns V[key][dim] for the key that
-//    the matching P^T slot holds (the S^T accumulator register it came from);
+//  * every O^T = V^T P^T operand, gathered by the modelled transposed read
+//    (lane i of a 16-lane group receives element i%4 of the row that lane
+//    4e + i/4 addressed), equals V[key][dim] for the key that the matching
+//    P^T slot holds (the S^T accumulator register it came from);
 //  * the accumulator row map and the P^T key map are bijections;
 //  * the workgroup order is a bijection onto (head, Q block) pairs.
+// It also reports LDS bank conflicts of the operand reads (informational).
 // Exit status 0 and "OK" on success; a message and status 1 otherwise.
 #include <cstdio>
 #include <cstdlib>
@@ -29,58 +32,113 @@ static int g_fail = 0;
         }                                      \
     } while (0)
 
-template <int D, int BC>
-void check_tile() {
+// LDS element map after DMA: element index (byte / 2) -> source element key*D + dim
+template <int D, int BC, bool IS_V>
+std::vector<int> dma_tile() {
     constexpr int CH = D / 8;
     constexpr int TILE = BC * D * 2;
-
-    // K staging: (key, chunk) -> 16-byte unit
-    std::vector<int> kown(TILE / 16, -1);
-    for (int key = 0; key < BC; ++key)
-        for (int ch = 0; ch < CH; ++ch) {
-            const int off = k_lds_offset<D>(key, ch);
-            CHECK(off >= 0 && off + 16 <= TILE && off % 16 == 0, "K write out of range D=%d BC=%d", D, BC);
-            if (off < 0 || off + 16 > TILE) continue;
-            CHECK(kown[off / 16] == -1, "K unit written twice D=%d BC=%d", D, BC);
-            kown[off / 16] = key * CH + ch;
+    std::vector<int> lds(TILE / 2, -1), seen(BC * D, 0);
+    for (int u = 0; u < BC * CH; ++u) {
+        const int src = IS_V ? v_dma_src_elem<D>(u) : k_dma_src_elem<D>(u);
+        CHECK(src >= 0 && src + 8 <= BC * D && src % 8 == 0, "DMA source chunk out of the tile");
+        if (src < 0 || src + 8 > BC * D) continue;
+        for (int e = 0; e < 8; ++e) {
+            lds[(16 * u + 2 * e) / 2] = src + e;
+            seen[src + e]++;
         }
-    for (int kb = 0; kb < BC / 32; ++kb)
-        for (int l32 = 0; l32 < 32; ++l32)
-            for (int g = 0; g < 2; ++g)
-                for (int ks = 0; ks < D / 16; ++ks) {
-                    const int off = k_operand_offset<D>(kb, l32, g, ks);
-                    CHECK(off >= 0 && off + 16 <= TILE, "K read out of range");
-                    if (off < 0 || off + 16 > TILE) continue;
-                    CHECK(kown[off / 16] == (32 * kb + l32) * CH + (2 * ks + g), "K read fetches the wrong chunk");
-                }
+    }
+    for (int i = 0; i < BC * D; ++i) CHECK(seen[i] == 1, "DMA does not place every element exactly once");
+    for (int key = 0; key < BC; ++key)
+        for (int dim = 0; dim < D; ++dim) {
+            const int off = IS_V ? v_elem_offset<D>(key, dim) : k_elem_offset<D>(key, dim);
+            CHECK(off >= 0 && off + 2 <= TILE, "element offset out of the tile");
+            if (off >= 0 && off + 2 <= TILE) CHECK(lds[off / 2] == key * D + dim, "element offset disagrees with DMA");
+        }
+    return lds;
+}
 
-    // V^T staging: element (key, dim) -> byte
-    std::vector<int> vown(TILE / 2, -1);
-    for (int u = 0; u < BC / 4; ++u)
-        for (int dc = 0; dc < CH; ++dc)
-            for (int e = 0; e < 8; ++e) {
-                const int dim = 8 * dc + e;
-                const int off = vt_lds_offset<BC>(dim, vt_slot_of_group(u));
-                CHECK(off >= 0 && off + 8 <= TILE && off % 8 == 0, "V write out of range D=%d BC=%d", D, BC);
-                if (off < 0 || off + 8 > TILE) continue;
-                for (int j = 0; j < 4; ++j) {
-                    const int el = (off + 2 * j) / 2;
-                    CHECK(vown[el] == -1, "V element written twice");
-                    vown[el] = (4 * u + j) * D + dim;
+// banks: 64 x 4 bytes; conflict degree of a set of (lane, byte range) accesses
+int bank_degree(const std::vector<std::pair<int, int>> &acc) {
+    std::vector<std::vector<int>> words(64);
+    for (auto &a : acc)
+        for (int b = a.first; b < a.first + a.second; b += 4) {
+            const int word = b / 4, bank = word % 64;
+            bool found = false;
+            for (int w : words[bank]) found |= (w == word);
+            if (!found) words[bank].push_back(word);
+        }
+    int deg = 0;
+    for (auto &w : words) deg = deg > (int)w.size() ? deg : (int)w.size();
+    return deg;
+}
+
+template <int D, int BC>
+void check_tile() {
+    constexpr int TILE = BC * D * 2;
+    std::vector<int> klds = dma_tile<D, BC, false>();
+    std::vector<int> vlds = dma_tile<D, BC, true>();
+    int kdeg = 0, vdeg = 0;
+
+    for (int kb = 0; kb < BC / 32; ++kb)
+        for (int ks = 0; ks < D / 16; ++ks) {
+            std::vector<std::pair<int, int>> phase;
+            for (int lane = 0; lane < 64; ++lane) {
+                const int l32 = lane & 31, g = lane >> 5;
+                const int off = k_operand_offset<D>(kb, l32, g, ks);
+                CHECK(off >= 0 && off + 16 <= TILE && off % 16 == 0, "K read out of range or misaligned");
+                if (off < 0 || off + 16 > TILE) continue;
+                for (int e = 0; e < 8; ++e)
+                    CHECK(klds[off / 2 + e] == (32 * kb + l32) * D + 16 * ks + 8 * g + e,
+                          "K operand fetches the wrong element D=%d", D);
+                phase.push_back({off, 16});
+                if (phase.size() == 8) {   // 16-byte reads: 8 lanes per 128-byte phase
+                    int d = bank_degree(phase);
+                    kdeg = kdeg > d ? kdeg : d;
+                    phase.clear();
                 }
             }
-    for (int i = 0; i < TILE / 2; ++i) CHECK(vown[i] != -1, "V^T tile has a hole");
+        }
+
     for (int db = 0; db < D / 32; ++db)
-        for (int l32 = 0; l32 < 32; ++l32)
-            for (int g = 0; g < 2; ++g)
-                for (int ks2 = 0; ks2 < BC / 16; ++ks2)
-                    for (int s = 0; s < 8; ++s) {
-                        const int off = v_operand_offset<BC>(db, l32, g, ks2, s >> 2) + 2 * (s & 3);
-                        CHECK(off >= 0 && off + 2 <= TILE, "V read out of range");
-                        if (off < 0 || off + 2 > TILE) continue;
-                        const int want = pv_key(ks2, g, s) * D + (32 * db + l32);
-                        CHECK(vown[off / 2] == want, "V read fetches the wrong element D=%d BC=%d", D, BC);
+        for (int ks2 = 0; ks2 < BC / 16; ++ks2)
+            for (int sh = 0; sh < 2; ++sh)
+                for (int G = 0; G < 4; ++G) {
+                    int addr[16];
+                    std::vector<std::pair<int, int>> phase;
+                    for (int j = 0; j < 16; ++j) {
+                        addr[j] = v_operand_tr_offset<D>(db, 16 * G + j, ks2, sh);
+                        CHECK(addr[j] >= 0 && addr[j] + 8 <= TILE && addr[j] % 8 == 0,
+                              "V transposed read out of range or misaligned");
+                        phase.push_back({addr[j], 8});
                     }
+                    int d = bank_degree(phase);
+                    vdeg = vdeg > d ? vdeg : d;
+                    for (int i = 0; i < 16; ++i)
+                        for (int e = 0; e < 4; ++e) {
+                            const int a = addr[tr_src_lane(i, e)];
+                            if (a < 0 || a + 8 > TILE) continue;
+                            const int got = vlds[a / 2 + tr_src_elem(i)];
+                            const int lane = 16 * G + i, g = lane >> 5, l32 = lane & 31;
+                            const int want = pv_key(ks2, g, 4 * sh + e) * D + (32 * db + l32);
+                            CHECK(got == want, "V operand fetches the wrong element D=%d BC=%d", D, BC);
+                        }
+                }
+    // the kernel hoists the lane-dependent part of each operand address out of
+    // the tile loop and adds the block / k-step part as a constant
+    for (int lane = 0; lane < 64; ++lane) {
+        const int l32 = lane & 31, g = lane >> 5;
+        for (int kb = 0; kb < BC / 32; ++kb)
+            for (int ks = 0; ks < D / 16; ++ks)
+                CHECK(k_operand_offset<D>(kb, l32, g, ks) == k_operand_offset<D>(0, l32, g, ks) + 32 * kb * D * 2,
+                      "K operand offset is not lane part + block constant");
+        for (int db = 0; db < D / 32; ++db)
+            for (int ks2 = 0; ks2 < BC / 16; ++ks2)
+                for (int sh = 0; sh < 2; ++sh)
+                    CHECK(v_operand_tr_offset<D>(db, lane, ks2, sh) ==
+                              v_operand_tr_offset<D>(db, lane, 0, 0) + (16 * ks2 + 8 * sh) * D * 2,
+                          "V operand offset is not lane part + k-step constant");
+    }
+    std::printf("D=%3d BC=%3d: K-operand bank conflict degree %d, V-operand %d\n", D, BC, kdeg, vdeg);
 }
 
 void check_maps() {
@@ -102,6 +160,11 @@ void check_maps() {
             }
         for (int i = 0; i < 16; ++i) CHECK(cnt[i] == 1, "pv_key not a bijection");
     }
+    // the transposed-read model is a bijection of the 16 x 4 block
+    std::vector<int> hit(64, 0);
+    for (int i = 0; i < 16; ++i)
+        for (int e = 0; e < 4; ++e) hit[4 * tr_src_lane(i, e) + tr_src_elem(i)]++;
+    for (int i = 0; i < 64; ++i) CHECK(hit[i] == 1, "transposed-read model not a bijection");
 }
 
 void check_workgroups() {
