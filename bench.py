@@ -159,6 +159,22 @@ def run_workload(name, steps, warmup, with_cpu, cpu_target_s):
     return rec
 
 
+def copy_probe(nbytes: int, steps: int) -> int:
+    """Plain copies of a known size: each reads and writes ``nbytes`` once."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"copy_bytes": src.numel() * 4, "steps": steps, "ms_per_copy": dt * 1e3,
+                      "GB/s_read_plus_write": 2 * src.numel() * 4 / dt / 1e9}), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,11 +183,16 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of attention, run --steps plain device-to-device copies of this many bytes "
+                         "(the reference kernel for calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this forward runs on one GPU; --gpus %d is not supported (use --gpus 1)" % args.gpus,
               file=sys.stderr)
         return 2
+    if args.copy_bytes:
+        return copy_probe(args.copy_bytes, args.steps)
     import fa_inputs
     names = list(fa_inputs.WORKLOADS) if args.workload == "all" else [args.workload]
     for i, name in enumerate(names):

@@ -55,15 +55,26 @@ FA_HD int pv_key(int ks2, int g, int s) { return 32 * (ks2 >> 1) + acc_row(8 * (
 
 // ---------------------------------------------------------------------------
 // Swizzles: LDS unit (key, pos) holds 8-dim chunk pos ^ f(key)
+//
+// Bank model: 64 banks of 4 bytes, 256 bytes served per cycle -- 16 lanes of
+// a 16-byte read or 32 lanes of an 8-byte read at a time.  R = 256 / row
+// bytes key rows share one 256-byte bank line.
 // ---------------------------------------------------------------------------
 template <int D>
-FA_HD int k_swizzle(int key) {   // spreads 8 consecutive keys of one chunk column
-    return key & 7 & (D / 8 - 1);
+FA_HD int k_swizzle(int key) {
+    // K operand read: 16 lanes = 16 consecutive keys, one chunk column; the
+    // XOR puts their 16 chunks at 16 distinct positions of the bank line
+    constexpr int CH = D / 8, R = 16 / CH;
+    return (key / R) & (CH - 1);
 }
 
 template <int D>
-FA_HD int v_swizzle(int key) {   // spreads the 4 keys x 2 chunks a transposed read touches
-    return (2 * (key & 3)) & (D / 8 - 1);
+FA_HD int v_swizzle(int key) {
+    // transposed V read: 32 lanes = 4 consecutive keys x 32 dims (4 chunks);
+    // the XOR moves each key's aligned group of 4 chunks to its own quarter
+    // of the bank line
+    constexpr int CH = D / 8, R = 16 / CH;
+    return (4 * ((key / R) & 3)) & (CH - 1);
 }
 
 // Byte offset of element (key, dim) of a K or V tile in LDS.

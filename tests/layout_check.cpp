@@ -12,7 +12,8 @@
 //    P^T slot holds (the S^T accumulator register it came from);
 //  * the accumulator row map and the P^T key map are bijections;
 //  * the workgroup order is a bijection onto (head, Q block) pairs.
-// It also reports LDS bank conflicts of the operand reads (informational).
+// It also checks that the operand reads are free of LDS bank conflicts under
+// a 64-bank, 256-bytes-per-cycle model (d = 64 and 128).
 // Exit status 0 and "OK" on success; a message and status 1 otherwise.
 #include <cstdio>
 #include <cstdlib>
@@ -91,7 +92,7 @@ void check_tile() {
                     CHECK(klds[off / 2 + e] == (32 * kb + l32) * D + 16 * ks + 8 * g + e,
                           "K operand fetches the wrong element D=%d", D);
                 phase.push_back({off, 16});
-                if (phase.size() == 8) {   // 16-byte reads: 8 lanes per 128-byte phase
+                if (phase.size() == 16) {  // 16-byte reads: 16 lanes per 256-byte cycle
                     int d = bank_degree(phase);
                     kdeg = kdeg > d ? kdeg : d;
                     phase.clear();
@@ -104,15 +105,18 @@ void check_tile() {
             for (int sh = 0; sh < 2; ++sh)
                 for (int G = 0; G < 4; ++G) {
                     int addr[16];
-                    std::vector<std::pair<int, int>> phase;
+                    std::vector<std::pair<int, int>> phase;   // 8-byte reads: 32 lanes per 256-byte cycle
+                    for (int j = 0; j < 32; ++j) {
+                        const int a32 = v_operand_tr_offset<D>(db, 16 * (G & 2) + j, ks2, sh);
+                        phase.push_back({a32, 8});
+                    }
+                    int d = bank_degree(phase);
+                    vdeg = vdeg > d ? vdeg : d;
                     for (int j = 0; j < 16; ++j) {
                         addr[j] = v_operand_tr_offset<D>(db, 16 * G + j, ks2, sh);
                         CHECK(addr[j] >= 0 && addr[j] + 8 <= TILE && addr[j] % 8 == 0,
                               "V transposed read out of range or misaligned");
-                        phase.push_back({addr[j], 8});
                     }
-                    int d = bank_degree(phase);
-                    vdeg = vdeg > d ? vdeg : d;
                     for (int i = 0; i < 16; ++i)
                         for (int e = 0; e < 4; ++e) {
                             const int a = addr[tr_src_lane(i, e)];
@@ -139,6 +143,7 @@ void check_tile() {
                           "V operand offset is not lane part + k-step constant");
     }
     std::printf("D=%3d BC=%3d: K-operand bank conflict degree %d, V-operand %d\n", D, BC, kdeg, vdeg);
+    if (D >= 64) CHECK(kdeg == 1 && vdeg == 1, "operand reads conflict under the 64-bank model D=%d BC=%d", D, BC);
 }
 
 void check_maps() {
