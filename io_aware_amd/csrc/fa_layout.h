@@ -136,9 +136,12 @@ FA_HD int tr_src_elem(int i) { return i & 3; }
 // Workgroup order.  Workgroup wg of nwg = BH * Tr goes to XCD wg % 8 in
 // dispatch order.  When nwg is a multiple of 8, XCD x receives the
 // contiguous work range [x * nwg/8, (x+1) * nwg/8), i.e. whole heads, so the
-// K/V of a head are read through one XCD's L2.  Within a head the Q blocks
-// run last-first under the causal mask (the last block does the most work).
-// The map is a bijection of [0, nwg) onto (bh, qblock) pairs.
+// K/V of a head are read through one XCD's L2.  Work is then taken two heads
+// at a time, alternating between the pair, with the Q blocks of each head
+// last-first under the causal mask: the longest blocks of the pair start
+// first and the short ones fill the tail, which balances the XCD's CUs
+// (list scheduling of decreasing lengths) while only two heads' K/V are in
+// use at once.  The map is a bijection of [0, nwg) onto (bh, qblock) pairs.
 // ---------------------------------------------------------------------------
 FA_HD void map_workgroup(int wg, int BH, int Tr, bool causal, int &bh, int &qblock) {
     const int nwg = BH * Tr;
@@ -147,8 +150,16 @@ FA_HD void map_workgroup(int wg, int BH, int Tr, bool causal, int &bh, int &qblo
         const int per_xcd = nwg >> 3;
         work = (wg & 7) * per_xcd + (wg >> 3);
     }
-    bh = work / Tr;
-    const int r = work - bh * Tr;
+    const int pair = work / (2 * Tr);
+    const int within = work - pair * 2 * Tr;
+    int r;
+    if (2 * pair + 1 < BH) {  // a full pair of heads: alternate between them
+        bh = 2 * pair + (within & 1);
+        r = within >> 1;
+    } else {                  // the last head of an odd count
+        bh = 2 * pair;
+        r = within;
+    }
     qblock = causal ? (Tr - 1 - r) : r;
 }
 

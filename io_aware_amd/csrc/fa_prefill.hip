@@ -30,10 +30,11 @@
 //  * Registers are budgeted for two waves per SIMD: a CU holds two
 //    independent workgroups whose MFMA and softmax phases overlap.
 //  * exp is computed as exp2 with scale*log2(e) folded into one FMA.
-//  * Lazy rescale: the accumulator is rescaled only when some row's max has
-//    grown by more than 2^8 (in the exp2 domain) over the max it is held
-//    against.  Until then P = exp2(s - m_held) <= 2^8, which float32 and the
-//    16-bit types hold without loss of relative precision; O and LSE are the
+//  * Lazy rescale: P is formed against the max the row is held at; the
+//    accumulator is rescaled (and the held max moved to the exact running
+//    max) only when some lane's tile sum of P exceeds 2^8.  Until then every
+//    P <= 2^8, which float32 and the 16-bit types hold without loss of
+//    relative precision, and no per-tile row max is needed; O and LSE are the
 //    same function of the inputs because acc, l and m always refer to the
 //    same held max.
 //  * Causal: K/V blocks after a workgroup's last query are never loaded;
@@ -41,7 +42,8 @@
 //    only blocks that cross the diagonal or the ragged key tail are masked.
 //    Rows of the ragged key tail are fetched from the last key (finite data
 //    that the mask removes), so no load leaves the tensor.
-//  * Workgroup order: whole heads per XCD, longest causal blocks first.
+//  * Workgroup order: whole heads per XCD, two heads interleaved, longest
+//    causal blocks first (fa_layout.h).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -103,8 +105,9 @@ struct PrefillArgs {
     float scale_log2;  // scale * log2(e)
 };
 
-// Held-max slack in the exp2 domain: P is at most 2^8 between rescales.
-constexpr float kRescaleSlack = 8.0f;
+// Bound on a lane's per-tile sum of P between rescales; it keeps every
+// P <= 2^8 (see the online-softmax step of prefill_kernel).
+constexpr float kHeldSumBound = 256.0f;
 constexpr float kLn2 = 0.693147180559945309417f;
 // word 3 of a raw buffer descriptor on gfx9-family parts
 constexpr int kBufferDword3 = 0x00020000;
@@ -272,52 +275,59 @@ void prefill_kernel(PrefillArgs a) {
         }
 
         // ---- online softmax -------------------------------------------------
+        // P = exp2(c*s - m_held) and its row sums are formed first.  A lane's
+        // tile sum <= 2^8 bounds each of its P by 2^8 (P >= 0), which is the
+        // lazy-rescale invariant, so the row max is only needed when some lane
+        // of the wave exceeds it (or has no held max yet).  Then the exact
+        // step runs on the untouched scores: m_new = max(m_held, rowmax),
+        // rescale acc and l by exp2(m_held - m_new), recompute P.
+        x8 pf[QB][KS2];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            float mx = -__builtin_inff();
+            auto exp_tile = [&](float msub) {
+                float lsum = 0.0f;
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+                for (int ks2 = 0; ks2 < KS2; ++ks2) {
+                    const int kb = ks2 >> 1;
+                    const int h = (ks2 & 1) * 8;
+                    f32x8 t;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[qb][kb][r]);
-            mx = xor32_max(mx);
-            const float mt = mx * c;  // block max in the exp2 domain (c > 0)
-            if (__ballot(mt > m_held[qb] + kRescaleSlack) != 0ull) {
-                const float m_new = __builtin_fmaxf(m_held[qb], mt);
+                    for (int e = 0; e < 8; ++e) {
+                        t[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][h + e], c, -msub));
+                        lsum += t[e];
+                    }
+                    pf[qb][ks2] = __builtin_convertvector(t, x8);
+                }
+                return lsum;
+            };
+            float lsum = 0.0f;
+            bool exact = __ballot(m_held[qb] == -__builtin_inff()) != 0ull;
+            if (!exact) {
+                lsum = exp_tile(m_held[qb]);
+                exact = __ballot(!(lsum <= kHeldSumBound)) != 0ull;  // also true for inf / NaN
+            }
+            if (exact) {
+                float mx = -__builtin_inff();
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[qb][kb][r]);
+                mx = xor32_max(mx);
+                const float m_new = __builtin_fmaxf(m_held[qb], mx * c);  // c > 0
                 const float alpha =
                     (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_held[qb] - m_new);
                 m_held[qb] = m_new;
                 l_part[qb] *= alpha;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha;
+                // a row that has seen no key yet keeps m = -inf: subtract 0
+                // there so masked scores give exp2(-inf) = 0, not NaN
+                lsum = exp_tile((m_new == -__builtin_inff()) ? 0.0f : m_new);
             }
-            // a row that has seen no key yet keeps m = -inf: subtract 0 there
-            // so masked scores give exp2(-inf) = 0, not NaN
-            const float msub = (m_held[qb] == -__builtin_inff()) ? 0.0f : m_held[qb];
-            float lsum = 0.0f;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][r], c, -msub));
-                    s[qb][kb][r] = p;
-                    lsum += p;
-                }
             l_part[qb] += lsum;
         }
 
         // ---- O^T += V^T P^T -------------------------------------------------
-        x8 pf[QB][KS2];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int ks2 = 0; ks2 < KS2; ++ks2) {
-                const int kb = ks2 >> 1;
-                const int h = (ks2 & 1) * 8;
-                f32x8 t;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) t[e] = s[qb][kb][h + e];
-                pf[qb][ks2] = __builtin_convertvector(t, x8);
-            }
 #pragma unroll
         for (int ks2 = 0; ks2 < KS2; ++ks2) {
 #pragma unroll
