@@ -4,10 +4,12 @@
 
 A step is one call of the forward (``fa_fwd``, or ``fa_fwd_splitkv`` for the
 decode workload) over one batch of seeded synthetic inputs already resident
-in device memory.  W untimed steps, then K timed steps bracketed by
-``torch.cuda.synchronize()``; each step is also bracketed by events on the
-stream the kernels run on, which gives the per-launch kernel time used for
-the roofline fraction.
+in device memory.  The GPU's clock ramps up over the first tens of
+milliseconds of sustained load after idle, so untimed steps run for at least
+``--prewarm-s`` seconds (0.3 by default) before the W untimed warmup steps;
+then K timed steps are bracketed by ``torch.cuda.synchronize()``.  Each step
+is also bracketed by events on the stream the kernels run on, which gives
+the per-launch kernel time used for the roofline fraction.
 
 The default workload is causal bf16 prefill, B=8, H=16, N=4096, d=128.
 FLOPs follow the convention 4*B*H*Nq*Nk*d (the two contractions), halved
@@ -93,7 +95,7 @@ def cpu_baseline(w, q, k, v, target_s: float):
                 rows_done, total_rows, rows_done, elapsed)}
 
 
-def run_workload(name, steps, warmup, with_cpu, cpu_target_s):
+def run_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s=0.3):
     import torch
     import fa_inputs
     import io_aware_amd as fa
@@ -114,6 +116,11 @@ def run_workload(name, steps, warmup, with_cpu, cpu_target_s):
         def step():
             fa.fa_fwd(qd, kd, vd, scale=w.scale, causal=w.causal, out=out, lse=lse)
 
+    t_end = time.perf_counter() + prewarm_s
+    while time.perf_counter() < t_end:   # clock ramp-up: untimed
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -147,7 +154,8 @@ def run_workload(name, steps, warmup, with_cpu, cpu_target_s):
     rec = {
         "metric": "attention fwd TFLOP/s (and % of MI355X bf16 MFMA/HBM roofline) per config",
         "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
-        "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, "higher_is_better": True, "scaling": "weak",
+        "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, "prewarm_s": prewarm_s,
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded randn, cast with RNE)",
         "config": {"workload": name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
                    "causal": w.causal, "dtype": w.dtype, "q_sigma": w.q_sigma, "num_splits": w.num_splits,
@@ -183,6 +191,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
+    ap.add_argument("--prewarm-s", type=float, default=0.3,
+                    help="seconds of untimed steps before the warmup steps (lets the GPU clock ramp up)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of attention, run --steps plain device-to-device copies of this many bytes "
                          "(the reference kernel for calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -198,7 +208,7 @@ def main():
     for i, name in enumerate(names):
         rec = run_workload(name, args.steps, args.warmup,
                            with_cpu=(not args.no_cpu_baseline) and (i == 0 or args.workload != "all"),
-                           cpu_target_s=args.cpu_seconds)
+                           cpu_target_s=args.cpu_seconds, prewarm_s=args.prewarm_s)
         print(json.dumps(rec), flush=True)
     return 0
 
