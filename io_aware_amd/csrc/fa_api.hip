@@ -80,11 +80,13 @@ size_t workspace_bytes(int B, int H, int Nq, int d, int S) {
     return (floats * sizeof(float) + 255) / 256 * 256;
 }
 
-// Prefill tile shape: the default, or FA_PREFILL_SHAPE (0, 1, 2) for sweeps.
-int prefill_shape() {
+// Prefill tile shape: FA_PREFILL_SHAPE (0 .. 3) for sweeps, else the
+// measured best for the head dim -- 32-key tiles at three waves per SIMD for
+// d = 128, 64-key tiles at two waves per SIMD below.
+int prefill_shape(int d) {
     const char *env = std::getenv("FA_PREFILL_SHAPE");
     if (env && env[0] >= '0' && env[0] < '0' + fa::kNumPrefillShapes && env[1] == '\0') return env[0] - '0';
-    return fa::kShapeW4Q32;
+    return d >= 128 ? fa::kShapeW4Q32B32 : fa::kShapeW4Q32;
 }
 
 // Library-owned decode workspaces, one per (device, stream).
@@ -151,7 +153,7 @@ int fa_fwd(const void *q, const void *k, const void *v, void *out, float *lse, i
         return hip_status(fa::launch_prefill_f32(d, causal == 1, q, k, v, out, lse, B * H, Nq, Nk, sl, stream),
                           "fp32 prefill launch");
     return hip_status(
-        fa::launch_prefill(dtype, d, causal == 1, prefill_shape(), q, k, v, out, lse, B * H, Nq, Nk, sl, stream),
+        fa::launch_prefill(dtype, d, causal == 1, prefill_shape(d), q, k, v, out, lse, B * H, Nq, Nk, sl, stream),
         "prefill launch");
 }
 

@@ -15,7 +15,8 @@ enum PrefillShape {
     kShapeW4Q32 = 0,   // 4 waves x 32 queries = Br 128, Bc 64
     kShapeW4Q64 = 1,   // 4 waves x 64 queries = Br 256, Bc 64
     kShapeW2Q64 = 2,   // 2 waves x 64 queries = Br 128, Bc 64
-    kNumPrefillShapes = 3
+    kShapeW4Q32B32 = 3,  // 4 waves x 32 queries = Br 128, Bc 32, three waves per SIMD
+    kNumPrefillShapes = 4
 };
 
 // Queries per workgroup (Br) of a prefill shape.

@@ -386,10 +386,9 @@ void prefill_kernel(PrefillArgs a) {
     }
 }
 
-template <typename T, int D, bool CAUSAL, int NW, int QW, int OCC>
+template <typename T, int D, bool CAUSAL, int NW, int QW, int OCC, int BC = 64>
 hipError_t launch_one(const void *q, const void *k, const void *v, void *out, float *lse, int BH, int Nq, int Nk,
                       float scale_log2, hipStream_t stream) {
-    constexpr int BC = 64;
     constexpr int BR = NW * QW;
     PrefillArgs a;
     a.q = q;
@@ -416,6 +415,9 @@ hipError_t launch_shape(int shape, const void *q, const void *k, const void *v, 
         case kShapeW4Q32: return launch_one<T, D, CAUSAL, 4, 32, 2>(q, k, v, out, lse, BH, Nq, Nk, sl, stream);
         case kShapeW4Q64: return launch_one<T, D, CAUSAL, 4, 64, 1>(q, k, v, out, lse, BH, Nq, Nk, sl, stream);
         case kShapeW2Q64: return launch_one<T, D, CAUSAL, 2, 64, 1>(q, k, v, out, lse, BH, Nq, Nk, sl, stream);
+        case kShapeW4Q32B32:  // a 32-key tile of d = 32 is too small to split over 256 threads
+            if constexpr (D >= 64) return launch_one<T, D, CAUSAL, 4, 32, 3, 32>(q, k, v, out, lse, BH, Nq, Nk, sl, stream);
+            else return launch_one<T, D, CAUSAL, 4, 32, 2>(q, k, v, out, lse, BH, Nq, Nk, sl, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -443,6 +445,7 @@ int prefill_block_rows(int shape) {
         case kShapeW4Q32: return 128;
         case kShapeW4Q64: return 256;
         case kShapeW2Q64: return 128;
+        case kShapeW4Q32B32: return 128;
         default: return 0;
     }
 }

@@ -135,7 +135,7 @@ def test_ragged_shapes(fa, dtype, d, causal):
         run_full(fa, B, H, Nq, Nk, d, dtype, causal, seed=100 + i + 10 * d)
 
 
-@pytest.mark.parametrize("shape_id", [0, 1, 2])
+@pytest.mark.parametrize("shape_id", [0, 1, 2, 3])
 def test_every_prefill_tile_shape(fa, shape_id, monkeypatch):
     monkeypatch.setenv("FA_PREFILL_SHAPE", str(shape_id))
     for d in (64, 128):
