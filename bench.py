@@ -90,9 +90,10 @@ def cpu_baseline(w, q, k, v, target_s: float):
         if dt >= target_s or n >= total_rows:
             break
         n = min(total_rows, max(n * 2, int(n * target_s / max(dt, 1e-3) * 1.1)))
+    what = ("all %d query rows" % total_rows if rows_done == total_rows else
+            "%d of %d query rows drawn uniformly (numpy seed %d)" % (rows_done, total_rows, rows_done))
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d query rows (uniform, seed %d), %.1f s, fp64 three-pass oracle" % (
-                rows_done, total_rows, rows_done, elapsed)}
+            "sample": "%s, %.1f s, fp64 three-pass oracle" % (what, elapsed)}
 
 
 def run_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s=0.3):
