@@ -2,9 +2,9 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|all]
 
-A step is one call of the forward (``fa_fwd``, or ``fa_fwd_splitkv`` for the
-decode workload) over one batch of seeded synthetic inputs already resident
-in device memory.  The GPU's clock ramps up over the first tens of
+A step is one call of the forward (``fa_fwd``; ``fa_fwd_splitkv`` for the
+decode workload; ``fa_fwd_paged_decode`` for the paged-cache decode) over one
+batch of seeded synthetic inputs already resident in device memory.  The GPU's clock ramps up over the first tens of
 milliseconds of sustained load after idle, so untimed steps run for at least
 ``--prewarm-s`` seconds (0.3 by default) before the W untimed warmup steps;
 then K timed steps are bracketed by ``torch.cuda.synchronize()``.  Each step
@@ -96,27 +96,10 @@ def cpu_baseline(w, q, k, v, target_s: float):
             "sample": "%s, %.1f s, fp64 three-pass oracle" % (what, elapsed)}
 
 
-def run_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s=0.3):
+def time_steps(step, steps, warmup, prewarm_s):
+    """(ms per step over the timed region, mean per-launch kernel ms)."""
     import torch
-    import fa_inputs
-    import io_aware_amd as fa
-
-    w = fa_inputs.WORKLOADS[name]
-    q, k, v = fa_inputs.make_workload(w)
     dev = torch.device("cuda:0")
-    qd, kd, vd = (t.to(dev).contiguous() for t in (q, k, v))
-    out = torch.empty_like(qd)
-    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
-    if w.num_splits:
-        ws = torch.empty(fa.fa_splitkv_workspace_bytes(w.B, w.H, w.Nq, w.d, w.num_splits), dtype=torch.uint8,
-                         device=dev)
-
-        def step():
-            fa.fa_fwd_splitkv(qd, kd, vd, w.num_splits, scale=w.scale, workspace=ws, out=out, lse=lse)
-    else:
-        def step():
-            fa.fa_fwd(qd, kd, vd, scale=w.scale, causal=w.causal, out=out, lse=lse)
-
     t_end = time.perf_counter() + prewarm_s
     while time.perf_counter() < t_end:   # clock ramp-up: untimed
         for _ in range(4):
@@ -136,9 +119,33 @@ def run_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s=0.3):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     launch_ms = [s.elapsed_time(e) for s, e in ev]
-    ms_per_step = wall * 1e3 / steps
-    kernel_ms = sum(launch_ms) / len(launch_ms)
+    return wall * 1e3 / steps, sum(launch_ms) / len(launch_ms)
 
+
+def run_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s=0.3):
+    import torch
+    import fa_inputs
+    import io_aware_amd as fa
+
+    if name in fa_inputs.PAGED_WORKLOADS:
+        return run_paged_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s)
+    w = fa_inputs.WORKLOADS[name]
+    q, k, v = fa_inputs.make_workload(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev).contiguous() for t in (q, k, v))
+    out = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    if w.num_splits:
+        ws = torch.empty(fa.fa_splitkv_workspace_bytes(w.B, w.H, w.Nq, w.d, w.num_splits), dtype=torch.uint8,
+                         device=dev)
+
+        def step():
+            fa.fa_fwd_splitkv(qd, kd, vd, w.num_splits, scale=w.scale, workspace=ws, out=out, lse=lse)
+    else:
+        def step():
+            fa.fa_fwd(qd, kd, vd, scale=w.scale, causal=w.causal, out=out, lse=lse)
+
+    ms_per_step, kernel_ms = time_steps(step, steps, warmup, prewarm_s)
     flops = workload_flops(w)
     nbytes = workload_bytes(w)
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -165,6 +172,69 @@ def run_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s=0.3):
     }
     if with_cpu:
         rec["cpu_baseline"] = cpu_baseline(w, q, k, v, cpu_target_s)
+    return rec
+
+
+def paged_cpu_baseline(w, q, kc, vc, table, lens, target_s: float):
+    """Time the fp64 paged oracle (gather, then three-pass attention) on a
+    prefix of the sequences."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    qf, kf, vf = (t.float() for t in (q, kc, vc))   # exact widening, outside the timing
+    n = 1
+    while True:
+        t0 = time.perf_counter()
+        oracle.paged_decode(qf, kf, vf, table, lens, w.scale, seqs=range(n), threads=threads)
+        dt = time.perf_counter() - t0
+        if dt >= target_s or n >= w.B:
+            break
+        n = min(w.B, max(n + 1, int(n * target_s / max(dt, 1e-3) * 1.1)))
+    keys = int(lens[:n].clamp(min=0).sum())
+    flops = 4.0 * w.H * w.d * keys
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "sequences 0..%d of %d (%d keys x %d heads), %.1f s, gather + fp64 three-pass oracle"
+                      % (n - 1, w.B, keys, w.H, dt)}
+
+
+def run_paged_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s):
+    import torch
+    import fa_inputs
+    import io_aware_amd as fa
+
+    w = fa_inputs.PAGED_WORKLOADS[name]
+    q, kc, vc, table, lens = fa_inputs.make_paged(w)
+    dev = torch.device("cuda:0")
+    qd, kcd, vcd, td, ld = (t.to(dev).contiguous() for t in (q, kc, vc, table, lens))
+    out = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.fa_splitkv_workspace_bytes(w.B, w.H, 1, w.d, w.num_splits), dtype=torch.uint8, device=dev)
+
+    def step():
+        fa.fa_fwd_paged_decode(qd, kcd, vcd, td, ld, w.num_splits, scale=w.scale, workspace=ws, out=out, lse=lse)
+
+    ms_per_step, kernel_ms = time_steps(step, steps, warmup, prewarm_s)
+    es = 2
+    keys = int(lens.clamp(min=0).sum())
+    flops = 4.0 * w.H * w.d * keys
+    nbytes = float(2 * es * w.H * w.d * keys + 2 * es * w.B * w.H * w.d + 4 * w.B * w.H
+                   + 4 * table.numel() + 4 * w.B)
+    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(name)}
+    rec = {
+        "metric": "attention fwd TFLOP/s (and % of MI355X bf16 MFMA/HBM roofline) per config",
+        "value": flops / (ms_per_step * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, "prewarm_s": prewarm_s,
+        "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded randn, shuffled block table)",
+        "config": {"workload": name, "B": w.B, "H": w.H, "d": w.d, "block_size": w.block_size,
+                   "max_len": w.max_len, "keys_total": keys, "num_blocks": int(kc.shape[0]),
+                   "num_splits": w.num_splits, "dtype": w.dtype, "flop_per_step": flops,
+                   "algorithmic_bytes_per_step": nbytes},
+        "roofline": roof,
+    }
+    if with_cpu:
+        rec["cpu_baseline"] = paged_cpu_baseline(w, q, kc, vc, table, lens, cpu_target_s)
     return rec
 
 
@@ -205,7 +275,8 @@ def main():
     if args.copy_bytes:
         return copy_probe(args.copy_bytes, args.steps)
     import fa_inputs
-    names = list(fa_inputs.WORKLOADS) if args.workload == "all" else [args.workload]
+    names = (list(fa_inputs.WORKLOADS) + list(fa_inputs.PAGED_WORKLOADS) if args.workload == "all"
+             else [args.workload])
     for i, name in enumerate(names):
         rec = run_workload(name, args.steps, args.warmup,
                            with_cpu=(not args.no_cpu_baseline) and (i == 0 or args.workload != "all"),

@@ -70,6 +70,103 @@ WORKLOADS = {
     ]
 }
 
+
+
+@dataclass(frozen=True)
+class PagedWorkload:
+    """Single-token decode over a paged K/V cache [num_blocks, H, block_size, d]."""
+    name: str
+    B: int
+    H: int
+    d: int
+    block_size: int
+    max_len: int                 # keys of the longest sequence; the table has ceil(max_len/block_size) columns
+    dtype: str
+    seed: int
+    num_splits: int
+    lens: str = "full"           # "full": every sequence max_len keys; "mixed": drawn lengths, edge cases included
+    hole_frac: float = 0.0       # fraction of a sequence's logical blocks left unallocated (table entry -1)
+    spare_blocks: int = 0        # physical blocks no table entry names
+    poison: bool = False         # fill every cache row no sequence reads with NaN
+    note: str = field(default="", compare=False)
+
+    @property
+    def scale(self) -> float:
+        return default_scale(self.d)
+
+    @property
+    def torch_dtype(self):
+        return DTYPES[self.dtype]
+
+
+PAGED_WORKLOADS = {
+    w.name: w for w in [
+        PagedWorkload(
+            "paged_decode_bf16_b16h32_len8192_d128_bs16_split32", 16, 32, 128, 16, 8192, "bf16", 1006, 32,
+            note="the decode workload's sizes with the cache in 16-key pages in shuffled order"),
+        PagedWorkload("paged_mixed_f16_b6h4_len1000_d64_bs16_split8", 6, 4, 64, 16, 1000, "f16", 1007, 8,
+                      lens="mixed", hole_frac=0.1, spare_blocks=5, poison=True),
+    ]
+}
+
+
+def make_paged(w: PagedWorkload):
+    """(q, k_cache, v_cache, block_table, seq_lens) on the CPU.
+
+    Recipe: a CPU generator seeded with ``w.seed`` draws, in order,
+    * the sequence lengths: all ``max_len`` ("full"), or ("mixed") the edge
+      lengths 0, 1, block_size - 1, block_size + 1 and max_len first, the rest
+      uniform in [1, max_len];
+    * a permutation of the physical blocks; each sequence takes its
+      ceil(len / block_size) logical blocks from it in order, so consecutive
+      logical blocks sit at unrelated physical places; unused table columns
+      are -1;
+    * with ``hole_frac`` > 0, that fraction of allocated table entries set to
+      -1 (unallocated: their keys are skipped);
+    * q [B, H, 1, d], then k_cache and v_cache [num_blocks, H, block_size, d],
+      standard normal in float32, rounded to the dtype (nearest-even).
+    With ``poison``, every cache row no sequence reads (spare blocks, rows of
+    a last block past the sequence end, blocks of holes) is set to NaN, so a
+    stray read shows up in the output.
+    """
+    g = torch.Generator().manual_seed(int(w.seed))
+    bs = w.block_size
+    max_blocks = -(-w.max_len // bs)
+    if w.lens == "full":
+        lens = [w.max_len] * w.B
+    else:
+        edge = [0, 1, bs - 1, bs + 1, w.max_len]
+        rest = torch.randint(1, w.max_len + 1, (w.B,), generator=g).tolist()
+        lens = [min(w.max_len, x) for x in (edge + rest)[:w.B]]
+    need = [-(-n // bs) for n in lens]
+    num_blocks = sum(need) + w.spare_blocks
+    perm = torch.randperm(max(num_blocks, 1), generator=g).tolist()
+    table = torch.full((w.B, max_blocks), -1, dtype=torch.int32)
+    pos = 0
+    for b in range(w.B):
+        for j in range(need[b]):
+            table[b, j] = perm[pos]
+            pos += 1
+    if w.hole_frac > 0:
+        drop = torch.rand((w.B, max_blocks), generator=g) < w.hole_frac
+        table[drop] = -1
+    q = torch.randn((w.B, w.H, 1, w.d), generator=g, dtype=torch.float32)
+    k = torch.randn((max(num_blocks, 1), w.H, bs, w.d), generator=g, dtype=torch.float32)
+    v = torch.randn((max(num_blocks, 1), w.H, bs, w.d), generator=g, dtype=torch.float32)
+    if w.poison:
+        used = torch.zeros((k.shape[0], bs), dtype=torch.bool)
+        for b in range(w.B):
+            for j in range(need[b]):
+                blk = int(table[b, j])
+                if blk >= 0:
+                    used[blk, :min(bs, lens[b] - j * bs)] = True
+        unread = ~used[:, None, :, None]
+        k.masked_fill_(unread, float("nan"))
+        v.masked_fill_(unread, float("nan"))
+    seq_lens = torch.tensor(lens, dtype=torch.int32)
+    return q.to(w.torch_dtype), k.to(w.torch_dtype), v.to(w.torch_dtype), table, seq_lens
+
+
 # The fp16 shapes of the Triton page's own test (seed 42, 2-D per-head inputs,
 # seqlen_q x seqlen_k x head_dim), run here as B = H = 1.
 TRITON_PAGE_SHAPES = [(256, 256, 64), (128, 256, 64), (64, 64, 32)]

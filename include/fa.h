@@ -116,6 +116,36 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *out,
                    int dtype, hipStream_t stream);
 
 /*
+ * fa_fwd_paged_decode -- single-token decode over a paged K/V cache
+ * ("6. FlashAttention 分块逻辑", section 12: the kernel walks a sequence's
+ * logical K/V blocks, finds each physical block through the block table and
+ * loads it directly, skipping an unallocated block).
+ *
+ * q: [B, H, 1, d]; k_cache, v_cache: [num_blocks, H, block_size, d] each (the
+ * page's [2, num_blocks, num_heads, block_size, head_dim] cache split into its
+ * K and V halves); block_table: int32 [B, max_blocks_per_seq], entry j of row
+ * b is the physical block holding sequence b's keys [j*block_size,
+ * (j+1)*block_size); seq_lens: int32 [B], the number of keys of each
+ * sequence.  All device pointers, element type ``dtype`` (fp16 or bf16) for
+ * q, the caches and out.  out: [B, H, 1, d]; lse: [B, H] float32 or NULL.
+ *
+ * A table entry outside [0, num_blocks) marks an unallocated block: its keys
+ * are skipped.  seq_lens are clamped to [0, max_blocks_per_seq*block_size];
+ * a sequence with no key gets O = 0 and LSE = -inf.  block_size: a power of
+ * two in [1, 1024].  The split is as in fa_fwd_splitkv, per sequence: chunks
+ * of ceil(len_b / num_splits) keys, 1 <= num_splits <= 1024.  workspace: at
+ * least fa_splitkv_workspace_bytes(B, H, 1, d, num_splits) bytes, 16-byte
+ * aligned.  Table and lengths must be 4-byte aligned; the other tensors
+ * 16-byte aligned.
+ */
+int fa_fwd_paged_decode(const void *q, const void *k_cache, const void *v_cache,
+                        const int *block_table, const int *seq_lens, void *out,
+                        float *lse, int B, int H, int d, int block_size,
+                        int max_blocks_per_seq, int num_blocks, float scale,
+                        int num_splits, void *workspace, size_t workspace_bytes,
+                        int dtype, hipStream_t stream);
+
+/*
  * fa_default_num_splits -- chunk count fa_fwd uses for a decode call:
  * ceil(Nk / 256) clamped to [1, 64] (8192 keys -> 32 chunks of 256).
  * Returns 0 if Nk < 1.

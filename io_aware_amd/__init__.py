@@ -32,6 +32,11 @@ _SIGNATURES = {
                                       ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p,
                                       ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]),
+    "fa_fwd_paged_decode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+                                           ctypes.c_int, ctypes.c_void_p]),
     "fa_default_num_splits": (ctypes.c_int, [ctypes.c_int]),
     "fa_release_workspace": (ctypes.c_int, []),
     "fa_map_workgroup": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -150,6 +155,44 @@ def fa_fwd_splitkv(q, k, v, num_splits, scale=None, workspace=None, out=None, ls
     return out, lse
 
 
+def fa_fwd_paged_decode(q, k_cache, v_cache, block_table, seq_lens, num_splits, scale=None, workspace=None,
+                        out=None, lse=None, return_lse=True, stream=None):
+    """Single-token decode over a paged cache.  q [B, H, 1, d]; k_cache and
+    v_cache [num_blocks, H, block_size, d]; block_table int32 [B, max_blocks];
+    seq_lens int32 [B].  Returns (out [B, H, 1, d], lse [B, H])."""
+    import torch
+    if q.dim() != 4 or q.shape[2] != 1:
+        raise ValueError("q must be [B, H, 1, d]")
+    B, H, _, d = q.shape
+    if k_cache.dim() != 4 or tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.shape[1] != H \
+            or k_cache.shape[3] != d:
+        raise ValueError("k_cache and v_cache must be [num_blocks, H, block_size, d]")
+    num_blocks, _, block_size, _ = k_cache.shape
+    if block_table.dim() != 2 or block_table.shape[0] != B or block_table.dtype != torch.int32:
+        raise ValueError("block_table must be int32 [B, max_blocks]")
+    if seq_lens.dim() != 1 or seq_lens.shape[0] != B or seq_lens.dtype != torch.int32:
+        raise ValueError("seq_lens must be int32 [B]")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("block_table", block_table),
+                    ("seq_lens", seq_lens)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous device tensor" % name)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = fa_splitkv_workspace_bytes(B, H, 1, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.fa_fwd_paged_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+                                   _ptr(out), _ptr(lse), B, H, d, block_size, block_table.shape[1], num_blocks,
+                                   float(scale), int(num_splits), _ptr(workspace), ws_bytes, _dtype_code(q),
+                                   _stream_handle(q, stream)), "fa_fwd_paged_decode")
+    return out, lse
+
+
 def fa_default_num_splits(Nk: int) -> int:
     return int(lib.fa_default_num_splits(Nk))
 
@@ -177,6 +220,6 @@ def fa_version() -> int:
     return int(lib.fa_version())
 
 
-__all__ = ["fa_fwd", "fa_fwd_splitkv", "fa_splitkv_workspace_bytes", "fa_default_num_splits",
+__all__ = ["fa_fwd", "fa_fwd_splitkv", "fa_fwd_paged_decode", "fa_splitkv_workspace_bytes", "fa_default_num_splits",
            "fa_release_workspace", "fa_map_workgroup", "fa_status_string", "fa_last_error", "fa_version",
            "FAError", "FA_F32", "FA_F16", "FA_BF16", "lib", "LIB_PATH"]

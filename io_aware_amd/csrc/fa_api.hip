@@ -184,6 +184,58 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *out, float
     return run_splitkv(q, k, v, out, lse, B, H, Nk, d, scale, num_splits, workspace, dtype, stream);
 }
 
+int fa_fwd_paged_decode(const void *q, const void *k_cache, const void *v_cache, const int *block_table,
+                        const int *seq_lens, void *out, float *lse, int B, int H, int d, int block_size,
+                        int max_blocks, int num_blocks, float scale, int num_splits, void *workspace,
+                        size_t ws_bytes, int dtype, hipStream_t stream) {
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out)
+        return fail(FA_ERR_INVALID_ARG, "q, k_cache, v_cache, block_table, seq_lens and out must be non-null");
+    if (B < 1 || H < 1 || d < 1 || block_size < 1 || max_blocks < 1 || num_blocks < 1)
+        return fail(FA_ERR_INVALID_ARG, "B, H, d, block_size, max_blocks_per_seq and num_blocks must be >= 1");
+    if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+    if (num_splits < 1 || num_splits > kMaxSplits)
+        return fail(FA_ERR_INVALID_ARG, "num_splits must be in [1, 1024]");
+    if (dtype != FA_F16 && dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "the paged path takes fp16 or bf16");
+    if (d != 32 && d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "d must be 32, 64 or 128");
+    if (block_size > 1024 || (block_size & (block_size - 1)) != 0)
+        return fail(FA_ERR_UNSUPPORTED, "block_size must be a power of two in [1, 1024]");
+    if ((int64_t)B * H > INT32_MAX || (int64_t)max_blocks * block_size > INT32_MAX ||
+        (int64_t)B * max_blocks > INT32_MAX || (int64_t)num_blocks * H > INT32_MAX)
+        return fail(FA_ERR_UNSUPPORTED, "B*H, max_blocks_per_seq*block_size, B*max_blocks_per_seq and "
+                                         "num_blocks*H must each fit in 31 bits");
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
+        return fail(FA_ERR_UNSUPPORTED, "q, k_cache, v_cache and out must be 16-byte aligned");
+    if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || (lse && !aligned(lse, 4)))
+        return fail(FA_ERR_UNSUPPORTED, "block_table, seq_lens and lse must be 4-byte aligned");
+    const size_t es = element_size(dtype);
+    const size_t bh = (size_t)B * H;
+    const size_t q_bytes = bh * d * es, cache_bytes = (size_t)num_blocks * H * block_size * d * es;
+    const size_t table_bytes = (size_t)B * max_blocks * 4, lens_bytes = (size_t)B * 4, lse_bytes = bh * 4;
+    const void *ins[5] = {q, k_cache, v_cache, block_table, seq_lens};
+    const size_t in_bytes[5] = {q_bytes, cache_bytes, cache_bytes, table_bytes, lens_bytes};
+    for (int i = 0; i < 5; ++i) {
+        if (overlaps(out, q_bytes, ins[i], in_bytes[i])) return fail(FA_ERR_INVALID_ARG, "out overlaps an input");
+        if (lse && overlaps(lse, lse_bytes, ins[i], in_bytes[i]))
+            return fail(FA_ERR_INVALID_ARG, "lse overlaps an input");
+    }
+    if (lse && overlaps(lse, lse_bytes, out, q_bytes)) return fail(FA_ERR_INVALID_ARG, "lse overlaps out");
+    const size_t need = workspace_bytes(B, H, 1, d, num_splits);
+    if (!workspace || !aligned(workspace, 16) || ws_bytes < need)
+        return fail(FA_ERR_WORKSPACE, "workspace must be 16-byte aligned and hold fa_splitkv_workspace_bytes() = " +
+                                          std::to_string(need) + " bytes");
+    for (int i = 0; i < 5; ++i)
+        if (overlaps(workspace, need, ins[i], in_bytes[i]))
+            return fail(FA_ERR_WORKSPACE, "workspace overlaps an input");
+    if (overlaps(workspace, need, out, q_bytes) || (lse && overlaps(workspace, need, lse, lse_bytes)))
+        return fail(FA_ERR_WORKSPACE, "workspace overlaps an output");
+    int log2_block = 0;
+    while ((1 << log2_block) < block_size) ++log2_block;
+    const float sl = (float)((double)scale * kLog2e);
+    return hip_status(fa::launch_paged_decode(dtype, d, q, k_cache, v_cache, block_table, seq_lens, out, lse, B, H,
+                                              log2_block, max_blocks, num_blocks, sl, num_splits, workspace, stream),
+                      "paged decode launch");
+}
+
 int fa_default_num_splits(int Nk) {
     if (Nk < 1) return 0;
     int s = (Nk + 255) / 256;

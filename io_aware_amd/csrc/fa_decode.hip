@@ -9,6 +9,11 @@
 // LSE = logsumexp_c lse_c and O = sum_c exp(lse_c - LSE) o~_c, which is the
 // same function as the page's sequential (m, l, o) merge.
 //
+// The same stage one also reads a paged K/V cache (section 12 of the same
+// page): keys are found through a per-sequence block table and each sequence
+// has its own length, so one launch serves a batch of decode requests of
+// different context lengths.
+//
 // The work is bound by HBM bandwidth (one pass over K and V, about 1 FLOP per
 // byte), so the design is about bytes in flight, not arithmetic:
 //  * a 256-thread workgroup reads its chunk as 16-byte loads; CH = d/8
@@ -43,10 +48,17 @@ struct SplitArgs {
     const void *v;
     float *ws_o;    // [BH, S, D] normalised chunk outputs
     float *ws_lse;  // [BH, S] chunk logsumexp (natural log)
-    int Nk;
+    int Nk;         // contiguous K/V: keys per (b, h)
     int S;
-    int chunk;      // keys per chunk = ceil(Nk / S)
+    int chunk;      // contiguous K/V: keys per chunk = ceil(Nk / S)
     float scale_log2;
+    // paged K/V (k, v are caches [num_blocks, H, block_size, D])
+    const int *block_table;  // [B, max_blocks]
+    const int *seq_lens;     // [B]
+    int H;
+    int log2_block;
+    int max_blocks;
+    int num_blocks;
 };
 
 struct CombineArgs {
@@ -77,7 +89,13 @@ __device__ __forceinline__ float hi_to_f32<_Float16>(uint32_t w) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
-template <typename T, int D>
+// Stage one.  PAGED selects where key j of (b, h) lives: contiguous K/V at
+// row (b*H + h)*Nk + j, or, for a paged cache ("6. FlashAttention 分块逻辑"
+// section 12), at row (blk*H + h)*block_size + j % block_size of physical
+// block blk = block_table[b][j / block_size].  A physical index outside
+// [0, num_blocks) marks an unallocated block: its keys are skipped, as the
+// page's kernel skips them.
+template <typename T, int D, bool PAGED>
 __global__ __launch_bounds__(kSplitThreads) void splitkv_partial_kernel(SplitArgs a) {
     constexpr int NT = kSplitThreads;
     constexpr int CH = D / 8;   // lanes per key row (16 bytes each)
@@ -94,13 +112,29 @@ __global__ __launch_bounds__(kSplitThreads) void splitkv_partial_kernel(SplitArg
     const int kl = tid / CH;
     const int bh = blockIdx.x / a.S;
     const int cidx = blockIdx.x - bh * a.S;
-    const int Nk = a.Nk;
-    const int kbeg = min(Nk, cidx * a.chunk);
-    const int kend = min(Nk, kbeg + a.chunk);
+    int len = a.Nk, chunk = a.chunk, b = 0, h = 0;
+    if (PAGED) {
+        b = bh / a.H;
+        h = bh - b * a.H;
+        len = min(max(a.seq_lens[b], 0), a.max_blocks << a.log2_block);  // never past the table
+        chunk = (len + a.S - 1) / a.S;
+    }
+    const int kbeg = min(len, cidx * chunk);
+    const int kend = min(len, kbeg + chunk);
     const float c = a.scale_log2;
+    const int bmask = (1 << a.log2_block) - 1;
+    const int *table = a.block_table + (size_t)b * a.max_blocks;
+    // element offset of key row j (relative to the K/V base + dc*8), or -1
+    auto row_of = [&](int j) -> long long {
+        if (!PAGED) return (long long)j * D;
+        const int blk = table[j >> a.log2_block];
+        if (blk < 0 || blk >= a.num_blocks) return -1;
+        return (((long long)blk * a.H + h) * (bmask + 1) + (j & bmask)) * D;
+    };
 
-    const T *kp = static_cast<const T *>(a.k) + (size_t)bh * Nk * D + dc * 8;
-    const T *vp = static_cast<const T *>(a.v) + (size_t)bh * Nk * D + dc * 8;
+    const size_t base_off = PAGED ? 0 : (size_t)bh * a.Nk * D;
+    const T *kp = static_cast<const T *>(a.k) + base_off + dc * 8;
+    const T *vp = static_cast<const T *>(a.v) + base_off + dc * 8;
     const u32x4 qraw = *reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.q) + (size_t)bh * D + dc * 8);
     float qv[8];
 #pragma unroll
@@ -117,17 +151,21 @@ __global__ __launch_bounds__(kSplitThreads) void splitkv_partial_kernel(SplitArg
 
     for (int base = kbeg; base < kend; base += KL * U) {
         u32x4 kx[U], vx[U];
+        long long roff[U];
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             const int key = base + kl + KL * i;
-            kx[i] = u32x4{0u, 0u, 0u, 0u};
-            if (key < kend) kx[i] = *reinterpret_cast<const u32x4 *>(kp + (size_t)key * D);
+            roff[i] = (key < kend) ? row_of(key) : -1;
         }
 #pragma unroll
         for (int i = 0; i < U; ++i) {
-            const int key = base + kl + KL * i;
+            kx[i] = u32x4{0u, 0u, 0u, 0u};
+            if (roff[i] >= 0) kx[i] = *reinterpret_cast<const u32x4 *>(kp + roff[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
             vx[i] = u32x4{0u, 0u, 0u, 0u};
-            if (key < kend) vx[i] = *reinterpret_cast<const u32x4 *>(vp + (size_t)key * D);
+            if (roff[i] >= 0) vx[i] = *reinterpret_cast<const u32x4 *>(vp + roff[i]);
         }
         float s[U];
         float mx = -__builtin_inff();
@@ -141,8 +179,7 @@ __global__ __launch_bounds__(kSplitThreads) void splitkv_partial_kernel(SplitArg
             }
 #pragma unroll
             for (int msk = CH / 2; msk > 0; msk >>= 1) dot += __shfl_xor(dot, msk);
-            const int key = base + kl + KL * i;
-            s[i] = (key < kend) ? dot * c : -__builtin_inff();
+            s[i] = (roff[i] >= 0) ? dot * c : -__builtin_inff();
             mx = __builtin_fmaxf(mx, s[i]);
         }
         const float m_new = __builtin_fmaxf(m_run, mx);
@@ -210,12 +247,17 @@ __global__ __launch_bounds__(256) void splitkv_combine_kernel(CombineArgs a) {
         for (int c = lane; c < S; c += 64) M = __builtin_fmaxf(M, lse_c[c]);
 #pragma unroll
         for (int msk = 32; msk > 0; msk >>= 1) M = __builtin_fmaxf(M, __shfl_xor(M, msk));
-        float L = 0.f;
-        for (int c = lane; c < S; c += 64) L += __builtin_amdgcn_exp2f((lse_c[c] - M) * kLog2e);
+        if (M == -__builtin_inff()) {  // no visible key in any chunk: O = 0, LSE = -inf
+            LSE = M;
+            for (int c = lane; c < S; c += 64) wts[wave][c] = 0.f;
+        } else {
+            float L = 0.f;
+            for (int c = lane; c < S; c += 64) L += __builtin_amdgcn_exp2f((lse_c[c] - M) * kLog2e);
 #pragma unroll
-        for (int msk = 32; msk > 0; msk >>= 1) L += __shfl_xor(L, msk);
-        LSE = M + __builtin_amdgcn_logf(L) * kLn2d;
-        for (int c = lane; c < S; c += 64) wts[wave][c] = __builtin_amdgcn_exp2f((lse_c[c] - LSE) * kLog2e);
+            for (int msk = 32; msk > 0; msk >>= 1) L += __shfl_xor(L, msk);
+            LSE = M + __builtin_amdgcn_logf(L) * kLn2d;
+            for (int c = lane; c < S; c += 64) wts[wave][c] = __builtin_amdgcn_exp2f((lse_c[c] - LSE) * kLog2e);
+        }
     }
     __syncthreads();  // reached by every wave
     if (!valid) return;
@@ -230,24 +272,15 @@ __global__ __launch_bounds__(256) void splitkv_combine_kernel(CombineArgs a) {
     if (lane == 0 && a.lse != nullptr) a.lse[row] = LSE;
 }
 
-template <typename T, int D>
-hipError_t launch_splitkv_typed(const void *q, const void *k, const void *v, void *out, float *lse, int BH,
-                                int Nk, float sl, int S, void *workspace, hipStream_t stream) {
-    float *ws_o = static_cast<float *>(workspace);
-    float *ws_lse = ws_o + (size_t)BH * S * D;
-    SplitArgs a;
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.ws_o = ws_o;
+template <typename T, int D, bool PAGED>
+hipError_t launch_splitkv_typed(const SplitArgs &base, void *out, float *lse, int BH, hipStream_t stream) {
+    SplitArgs a = base;
+    float *ws_o = a.ws_o;
+    float *ws_lse = ws_o + (size_t)BH * a.S * D;
     a.ws_lse = ws_lse;
-    a.Nk = Nk;
-    a.S = S;
-    a.chunk = (Nk + S - 1) / S;
-    a.scale_log2 = sl;
-    const long long nwg = (long long)BH * S;
-    if (nwg > 0x7fffffffLL || S > kMaxSplits) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((splitkv_partial_kernel<T, D>), dim3((unsigned)nwg), dim3(kSplitThreads), 0, stream, a);
+    const long long nwg = (long long)BH * a.S;
+    if (nwg > 0x7fffffffLL || a.S > kMaxSplits) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((splitkv_partial_kernel<T, D, PAGED>), dim3((unsigned)nwg), dim3(kSplitThreads), 0, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     CombineArgs b;
@@ -256,31 +289,61 @@ hipError_t launch_splitkv_typed(const void *q, const void *k, const void *v, voi
     b.out = out;
     b.lse = lse;
     b.rows = BH;
-    b.S = S;
+    b.S = a.S;
     hipLaunchKernelGGL((splitkv_combine_kernel<T, D>), dim3((BH + 3) / 4), dim3(256), 0, stream, b);
     return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_splitkv_d(int d, const void *q, const void *k, const void *v, void *out, float *lse, int BH,
-                            int Nk, float sl, int S, void *ws, hipStream_t stream) {
+template <bool PAGED>
+hipError_t launch_any(int dtype, int d, const SplitArgs &a, void *out, float *lse, int BH, hipStream_t stream) {
+#define FA_CASE(DD)                                                                                 \
+    case DD:                                                                                        \
+        return dtype == 2 ? launch_splitkv_typed<__bf16, DD, PAGED>(a, out, lse, BH, stream)        \
+                          : launch_splitkv_typed<_Float16, DD, PAGED>(a, out, lse, BH, stream);
+    if (dtype != 1 && dtype != 2) return hipErrorInvalidValue;
     switch (d) {
-        case 32: return launch_splitkv_typed<T, 32>(q, k, v, out, lse, BH, Nk, sl, S, ws, stream);
-        case 64: return launch_splitkv_typed<T, 64>(q, k, v, out, lse, BH, Nk, sl, S, ws, stream);
-        case 128: return launch_splitkv_typed<T, 128>(q, k, v, out, lse, BH, Nk, sl, S, ws, stream);
+        FA_CASE(32)
+        FA_CASE(64)
+        FA_CASE(128)
         default: return hipErrorInvalidValue;
     }
+#undef FA_CASE
 }
 
 }  // namespace
 
 hipError_t launch_splitkv(int dtype, int d, const void *q, const void *k, const void *v, void *out, float *lse,
                           int BH, int Nk, float scale_log2, int num_splits, void *workspace, hipStream_t stream) {
-    if (dtype == 2)
-        return launch_splitkv_d<__bf16>(d, q, k, v, out, lse, BH, Nk, scale_log2, num_splits, workspace, stream);
-    if (dtype == 1)
-        return launch_splitkv_d<_Float16>(d, q, k, v, out, lse, BH, Nk, scale_log2, num_splits, workspace, stream);
-    return hipErrorInvalidValue;
+    SplitArgs a = {};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.ws_o = static_cast<float *>(workspace);
+    a.Nk = Nk;
+    a.S = num_splits;
+    a.chunk = (Nk + num_splits - 1) / num_splits;
+    a.scale_log2 = scale_log2;
+    return launch_any<false>(dtype, d, a, out, lse, BH, stream);
+}
+
+hipError_t launch_paged_decode(int dtype, int d, const void *q, const void *k_cache, const void *v_cache,
+                               const int *block_table, const int *seq_lens, void *out, float *lse, int B, int H,
+                               int log2_block, int max_blocks, int num_blocks, float scale_log2, int num_splits,
+                               void *workspace, hipStream_t stream) {
+    SplitArgs a = {};
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.ws_o = static_cast<float *>(workspace);
+    a.S = num_splits;
+    a.scale_log2 = scale_log2;
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.H = H;
+    a.log2_block = log2_block;
+    a.max_blocks = max_blocks;
+    a.num_blocks = num_blocks;
+    return launch_any<true>(dtype, d, a, out, lse, B * H, stream);
 }
 
 }  // namespace fa

@@ -41,4 +41,12 @@ hipError_t launch_splitkv(int dtype, int d, const void *q, const void *k,
                           float scale_log2, int num_splits, void *workspace,
                           hipStream_t stream);
 
+// Split-KV decode over a paged cache: k_cache, v_cache are
+// [num_blocks, H, block_size, d]; block_table [B, max_blocks] int32;
+// seq_lens [B] int32; block_size = 1 << log2_block.
+hipError_t launch_paged_decode(int dtype, int d, const void *q, const void *k_cache, const void *v_cache,
+                               const int *block_table, const int *seq_lens, void *out, float *lse, int B, int H,
+                               int log2_block, int max_blocks, int num_blocks, float scale_log2, int num_splits,
+                               void *workspace, hipStream_t stream);
+
 }  // namespace fa

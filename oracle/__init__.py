@@ -14,6 +14,10 @@ Two parts:
   otherwise, and returns O and LSE = m + ln(l).  Sources: "6. FlashAttention
   分块逻辑" (lowentro.cn) sections 1.1 and 4.1; "9.4 FlashAttention 与
   FlashMLA" (llm-fullstack-book) sections 9.4.2 and 9.4.5.
+* ``paged_decode`` -- single-token attention over a paged K/V cache: the keys
+  a sequence's block table maps (unallocated blocks dropped) are gathered in
+  logical order into a contiguous K/V, which ``attention`` then takes.
+  Source: "6. FlashAttention 分块逻辑" section 12.
 * ``oracle.algorithms`` -- the pages' algorithms (one-pass online softmax,
   blocked forward with deferred or per-step normalisation, split-KV partials
   and their merge) in numpy fp64.  They exist to pin ``attention`` and each
@@ -128,3 +132,65 @@ def visible_keys(Nq: int, Nk: int, causal: bool, rows) -> np.ndarray:
     if not causal:
         return np.full(i.shape, Nk, dtype=np.int64)
     return np.minimum(i + 1, Nk)
+
+
+def paged_gather_index(block_table, seq_len: int, block_size: int, num_blocks: int):
+    """(physical block, row in block) of each key a sequence sees, in logical
+    order ("6. FlashAttention 分块逻辑", section 12.2).
+
+    Logical block j of the sequence holds its keys [j*block_size,
+    (j+1)*block_size); the table row maps it to a physical block.  A negative
+    entry marks an unallocated block, whose keys are skipped; an entry
+    >= num_blocks is taken as unallocated too (it names no block of the
+    cache).  Only the first min(block_size, seq_len - j*block_size) rows of
+    the last block hold keys.  ``seq_len`` is clamped to [0, len(row) *
+    block_size].
+    """
+    row = np.asarray(block_table, dtype=np.int64).reshape(-1)
+    n = max(0, min(int(seq_len), row.size * block_size))
+    blks, offs = [], []
+    for j in range(-(-n // block_size)):
+        phys = int(row[j])
+        if phys < 0 or phys >= num_blocks:
+            continue
+        valid = min(block_size, n - j * block_size)
+        blks.extend([phys] * valid)
+        offs.extend(range(valid))
+    return np.array(blks, dtype=np.int64), np.array(offs, dtype=np.int64)
+
+
+def paged_decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, seqs=None, threads: int = 0):
+    """Exact single-token attention over a paged cache, in fp64.
+
+    q: [B, H, 1, d]; k_cache, v_cache: [num_blocks, H, block_size, d];
+    block_table: [B, max_blocks] integers; seq_lens: [B].  Each sequence's
+    keys (``paged_gather_index``) are gathered into K_b, V_b of shape
+    [1, H, n_b, d] and passed with q[b] to ``attention``.  A sequence with no
+    key gets O = 0 and LSE = -inf.  ``seqs`` selects sequences (all if None).
+
+    Returns (out [len(seqs), H, d], lse [len(seqs), H]), float64.
+    """
+    num_blocks, H, block_size, d = tuple(k_cache.shape)
+    table = np.asarray(block_table.cpu() if hasattr(block_table, "cpu") else block_table, dtype=np.int64)
+    lens = np.asarray(seq_lens.cpu() if hasattr(seq_lens, "cpu") else seq_lens, dtype=np.int64).reshape(-1)
+    B = table.shape[0]
+    seqs = list(range(B)) if seqs is None else [int(s) for s in seqs]
+    out = np.zeros((len(seqs), H, d), dtype=np.float64)
+    lse = np.full((len(seqs), H), -np.inf, dtype=np.float64)
+    for i, b in enumerate(seqs):
+        blks, offs = paged_gather_index(table[b], int(lens[b]), block_size, num_blocks)
+        if blks.size == 0:
+            continue
+        if hasattr(k_cache, "detach"):
+            import torch
+            bi, oi = torch.from_numpy(blks), torch.from_numpy(offs)
+        else:
+            bi, oi = blks, offs
+        # [n, H, d] -> [1, H, n, d]
+        kb = _as_f32(k_cache[bi, :, oi, :]).transpose(1, 0, 2)[None]
+        vb = _as_f32(v_cache[bi, :, oi, :]).transpose(1, 0, 2)[None]
+        qb = _as_f32(q[b:b + 1])
+        o, l = attention(qb, np.ascontiguousarray(kb), np.ascontiguousarray(vb), scale, False, threads=threads)
+        out[i] = o[0, :, 0, :]
+        lse[i] = l[0, :, 0]
+    return out, lse

@@ -304,3 +304,44 @@ def wrong_merge(parts):
         l = l + part["l"] * math.exp(part["m"] - m)
         o = o + part["o"] * math.exp(part["m"] - m)
     return o / l
+
+
+# --------------------------------------------------------------------------
+# Paged K/V cache
+# --------------------------------------------------------------------------
+
+def paged_attention_blocked(q, k_cache, v_cache, block_table, seq_len: int, scale: float):
+    """Attention of one query row over a paged cache, block by block, in the
+    order the page gives ("6. FlashAttention 分块逻辑", section 12.2): for each
+    logical block, look up its physical block in the table and skip it if it
+    is unallocated (negative; here also >= the number of physical blocks);
+    take its valid rows (all but the last block are full); form the scaled
+    scores; update the running max, the running sum and the rescaled
+    accumulator with the online rule; after the last block divide by the sum.
+
+    q [d]; k_cache, v_cache [num_blocks, block_size, d] (one head);
+    block_table [max_blocks].  Returns (o, lse); a row with no key gives
+    (0, -inf), where the page's final division would be 0/0.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k_cache = np.asarray(k_cache, dtype=np.float64)
+    v_cache = np.asarray(v_cache, dtype=np.float64)
+    table = np.asarray(block_table, dtype=np.int64).reshape(-1)
+    num_blocks, block_size, d = k_cache.shape
+    n = max(0, min(int(seq_len), table.size * block_size))
+    m, l, o = NEG_INF, 0.0, np.zeros(d)
+    for lb in range(-(-n // block_size)):
+        phys = int(table[lb])
+        if phys < 0 or phys >= num_blocks:
+            continue
+        valid = min(block_size, n - lb * block_size)
+        s = (k_cache[phys, :valid] @ q) * scale
+        m_new = max(m, float(s.max()))
+        factor = math.exp(m - m_new)
+        p = np.exp(s - m_new)
+        l = l * factor + float(p.sum())
+        o = o * factor + p @ v_cache[phys, :valid]
+        m = m_new
+    if l == 0.0:
+        return np.zeros(d), NEG_INF
+    return o / l, m + math.log(l)

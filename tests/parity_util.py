@@ -1,0 +1,38 @@
+"""Shared helpers of the GPU parity tests: the tolerances and the
+element-by-element comparison against the fp64 oracle.
+
+Tolerances on O and LSE (absolute, after widening the GPU outputs to fp64):
+float32 path max |dO| <= 1e-5; fp16 / bf16 paths max |dO| <= 2e-2 and
+mean |dO| <= 2e-3; LSE max |dLSE| <= 1e-3 on every path.
+"""
+import sys
+
+import numpy as np
+
+TOL = {"f32": (1e-5, None), "f16": (2e-2, 2e-3), "bf16": (2e-2, 2e-3)}
+LSE_TOL = 1e-3
+DEV = "cuda:0"
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def compare(out, lse, ref_o, ref_l, dtype, label):
+    o = out.detach().float().cpu().numpy().astype(np.float64).reshape(ref_o.shape)
+    l = lse.detach().float().cpu().numpy().astype(np.float64).reshape(ref_l.shape)
+    assert np.isfinite(o).all(), label + ": non-finite O"
+    assert np.isfinite(l).all(), label + ": non-finite LSE"
+    err = np.abs(o - ref_o)
+    lerr = np.abs(l - ref_l)
+    max_tol, mean_tol = TOL[dtype]
+    note("%s: max|dO|=%.3e mean|dO|=%.3e max|dLSE|=%.3e" % (label, err.max(), err.mean(), lerr.max()))
+    assert err.max() <= max_tol, "%s: max|dO| %.3e > %.1e" % (label, err.max(), max_tol)
+    if mean_tol is not None:
+        assert err.mean() <= mean_tol, "%s: mean|dO| %.3e > %.1e" % (label, err.mean(), mean_tol)
+    assert lerr.max() <= LSE_TOL, "%s: max|dLSE| %.3e > %.1e" % (label, lerr.max(), LSE_TOL)
+
+
+def to_dev(*ts):
+    return [t.to(DEV).contiguous() for t in ts]

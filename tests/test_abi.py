@@ -39,7 +39,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for want in ("fa_fwd", "fa_fwd_splitkv", "fa_splitkv_workspace_bytes", "fa_status_string",
+    for want in ("fa_fwd", "fa_fwd_splitkv", "fa_fwd_paged_decode", "fa_splitkv_workspace_bytes", "fa_status_string",
                  "fa_last_error", "fa_release_workspace", "fa_default_num_splits", "fa_map_workgroup"):
         assert want in names
 
@@ -167,3 +167,42 @@ def test_workgroup_order_groups_heads_by_xcd(fa):
     # causal: the first workgroup of a head takes its last (longest) block
     assert fa.fa_map_workgroup(0, BH, Tr, True) == (0, Tr - 1)
     assert fa.fa_map_workgroup(0, BH, Tr, False) == (0, 0)
+
+
+# fake addresses for the paged entry point: caches, table and lengths far apart
+KC, VC, TB, SL = (0x10000000 * i for i in range(8, 12))
+PGOOD = dict(q=Q, kc=KC, vc=VC, table=TB, lens=SL, out=O, lse=L, B=4, H=8, d=128, bs=16, max_blocks=64,
+             num_blocks=256, scale=0.125, S=8, ws=W, dtype=2)
+
+
+def call_paged(fa, ws_bytes=None, **over):
+    a = dict(PGOOD)
+    a.update(over)
+    if ws_bytes is None:
+        ws_bytes = fa.fa_splitkv_workspace_bytes(a["B"], a["H"], 1, a["d"], max(1, min(a["S"], 1024)))
+    return fa.lib.fa_fwd_paged_decode(a["q"], a["kc"], a["vc"], a["table"], a["lens"], a["out"], a["lse"],
+                                      a["B"], a["H"], a["d"], a["bs"], a["max_blocks"], a["num_blocks"],
+                                      a["scale"], a["S"], a["ws"], ws_bytes, a["dtype"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), 1), (dict(kc=None), 1), (dict(vc=None), 1), (dict(table=None), 1), (dict(lens=None), 1),
+    (dict(out=None), 1), (dict(B=0), 1), (dict(H=0), 1), (dict(bs=0), 1), (dict(max_blocks=0), 1),
+    (dict(num_blocks=0), 1), (dict(scale=0.0), 1), (dict(scale=math.nan), 1), (dict(S=0), 1), (dict(S=1025), 1),
+    (dict(dtype=0), 2), (dict(dtype=5), 2), (dict(d=96), 2),
+    (dict(bs=12), 2), (dict(bs=2048), 2),
+    (dict(max_blocks=1 << 27, bs=32), 2), (dict(num_blocks=1 << 29), 2),
+    (dict(q=Q + 8), 2), (dict(kc=KC + 4), 2), (dict(table=TB + 2), 2), (dict(lens=SL + 1), 2),
+    (dict(lse=L + 2), 2),
+    (dict(out=KC + 4096), 1), (dict(lse=TB), 1), (dict(lse=O + 16), 1), (dict(out=SL), 1),
+    (dict(ws=None), 4), (dict(ws=W + 8), 4), (dict(ws=VC + 1024), 4), (dict(ws=O), 4),
+])
+def test_paged_decode_rejects_invalid_arguments(fa, over, code):
+    assert call_paged(fa, **over) == code
+    assert fa.fa_last_error() != ""
+
+
+def test_paged_decode_rejects_small_workspace(fa):
+    need = fa.fa_splitkv_workspace_bytes(4, 8, 1, 128, 8)
+    assert call_paged(fa, ws_bytes=need - 1) == 4
+    assert "workspace" in fa.fa_last_error()

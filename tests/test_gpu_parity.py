@@ -24,39 +24,13 @@ import oracle
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": (1e-5, None), "f16": (2e-2, 2e-3), "bf16": (2e-2, 2e-3)}
-LSE_TOL = 1e-3
-DEV = "cuda:0"
+from parity_util import DEV, LSE_TOL, TOL, compare, note, to_dev  # noqa: E402
 
 
 @pytest.fixture(scope="module")
 def fa():
     import io_aware_amd
     return io_aware_amd
-
-
-def note(msg):
-    print(msg, flush=True)
-    sys.stdout.flush()
-
-
-def compare(out, lse, ref_o, ref_l, dtype, label):
-    o = out.detach().float().cpu().numpy().astype(np.float64).reshape(ref_o.shape)
-    l = lse.detach().float().cpu().numpy().astype(np.float64).reshape(ref_l.shape)
-    assert np.isfinite(o).all(), label + ": non-finite O"
-    assert np.isfinite(l).all(), label + ": non-finite LSE"
-    err = np.abs(o - ref_o)
-    lerr = np.abs(l - ref_l)
-    max_tol, mean_tol = TOL[dtype]
-    note("%s: max|dO|=%.3e mean|dO|=%.3e max|dLSE|=%.3e" % (label, err.max(), err.mean(), lerr.max()))
-    assert err.max() <= max_tol, "%s: max|dO| %.3e > %.1e" % (label, err.max(), max_tol)
-    if mean_tol is not None:
-        assert err.mean() <= mean_tol, "%s: mean|dO| %.3e > %.1e" % (label, err.mean(), mean_tol)
-    assert lerr.max() <= LSE_TOL, "%s: max|dLSE| %.3e > %.1e" % (label, lerr.max(), LSE_TOL)
-
-
-def to_dev(*ts):
-    return [t.to(DEV).contiguous() for t in ts]
 
 
 def run_full(fa, B, H, Nq, Nk, d, dtype, causal, seed, q_sigma=1.0, label=None):
