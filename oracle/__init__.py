@@ -14,6 +14,12 @@ Two parts:
   otherwise, and returns O and LSE = m + ln(l).  Sources: "6. FlashAttention
   分块逻辑" (lowentro.cn) sections 1.1 and 4.1; "9.4 FlashAttention 与
   FlashMLA" (llm-fullstack-book) sections 9.4.2 and 9.4.5.
+* ``attention_bwd`` -- the gradients dQ, dK, dV of exact attention for an
+  upstream gradient dO (``attn_bwd_oracle.c``): P from the three-pass
+  definition, dV = P^T dO, dP = dO V^T, D = rowsum(dO * O), dS = P * (dP - D),
+  dQ = scale dS K, dK = scale dS^T Q, in IEEE double.  Sources: "6.
+  FlashAttention 分块逻辑" section 7.1; "9.4 FlashAttention 与 FlashMLA"
+  section 9.4.5.
 * ``paged_decode`` -- single-token attention over a paged K/V cache: the keys
   a sequence's block table maps (unallocated blocks dropped) are gathered in
   logical order into a contiguous K/V, which ``attention`` then takes.
@@ -32,7 +38,7 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "attn_oracle.c")
+_SRCS = [os.path.join(_HERE, "attn_oracle.c"), os.path.join(_HERE, "attn_bwd_oracle.c")]
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
@@ -46,8 +52,7 @@ def build(force: bool = True) -> str:
     if not force and os.path.exists(_LIB_PATH):
         return _LIB_PATH
     tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-fopenmp", "-std=c99", "-Wall", "-shared", "-fPIC",
-           _SRC, "-o", tmp, "-lm"]
+    cmd = ["gcc", "-O2", "-fopenmp", "-std=c99", "-Wall", "-shared", "-fPIC"] + _SRCS + ["-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB_PATH)
     _lib = None
@@ -68,6 +73,13 @@ def _load():
         ctypes.c_int64, ctypes.c_double, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_int64,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    lib.oracle_attention_bwd.restype = ctypes.c_int
+    lib.oracle_attention_bwd.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_double, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
     lib.oracle_default_threads.restype = ctypes.c_int
     lib.oracle_default_threads.argtypes = []
     _lib = lib
@@ -194,3 +206,41 @@ def paged_decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, seqs=
         out[i] = o[0, :, 0, :]
         lse[i] = l[0, :, 0]
     return out, lse
+
+
+def attention_bwd(q, k, v, dout, scale: float, causal: bool, heads=None, q_idx=None, k_idx=None,
+                  threads: int = 0, with_delta: bool = False):
+    """Exact gradients of attention in fp64 for [B, H, N, d] inputs.
+
+    ``heads`` selects flat (b*H + h) heads (all if None); ``q_idx`` the query
+    indices within a head whose dQ is wanted (all if None); ``k_idx`` the key
+    indices for dK and dV (all if None).  Returns (dq, dk, dv) shaped
+    [nheads, nq, d], [nheads, nk, d], [nheads, nk, d] -- reshaped to
+    [B, H, N, d] when all three selections are None -- and, with
+    ``with_delta``, D_i = dO_i . O_i as [nheads, Nq] ([B, H, Nq]).
+    """
+    qa, ka, va, ga = _as_f32(q), _as_f32(k), _as_f32(v), _as_f32(dout)
+    B, H, Nq, d = qa.shape
+    Nk = ka.shape[2]
+    if ka.shape != (B, H, Nk, d) or va.shape != ka.shape or ga.shape != qa.shape:
+        raise ValueError("shape mismatch")
+    sel = [None if x is None else np.ascontiguousarray(x, dtype=np.int64) for x in (heads, q_idx, k_idx)]
+    nh = B * H if sel[0] is None else sel[0].size
+    nq = Nq if sel[1] is None else sel[1].size
+    nk = Nk if sel[2] is None else sel[2].size
+    dq = np.empty((nh, nq, d), dtype=np.float64)
+    dk = np.empty((nh, nk, d), dtype=np.float64)
+    dv = np.empty((nh, nk, d), dtype=np.float64)
+    delta = np.empty((nh, Nq), dtype=np.float64)
+    ptr = [None if x is None else x.ctypes.data for x in sel]
+    rc = _load().oracle_attention_bwd(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, ga.ctypes.data,
+                                      B, H, Nq, Nk, d, float(scale), 1 if causal else 0,
+                                      ptr[0], nh, ptr[1], nq, ptr[2], nk,
+                                      dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, delta.ctypes.data,
+                                      int(threads))
+    if rc != 0:
+        raise RuntimeError("oracle_attention_bwd failed with code %d" % rc)
+    if all(x is None for x in sel):
+        dq, dk, dv = dq.reshape(B, H, Nq, d), dk.reshape(B, H, Nk, d), dv.reshape(B, H, Nk, d)
+        delta = delta.reshape(B, H, Nq)
+    return (dq, dk, dv, delta) if with_delta else (dq, dk, dv)

@@ -345,3 +345,76 @@ def paged_attention_blocked(q, k_cache, v_cache, block_table, seq_len: int, scal
     if l == 0.0:
         return np.zeros(d), NEG_INF
     return o / l, m + math.log(l)
+
+
+# --------------------------------------------------------------------------
+# Backward by recomputation
+# --------------------------------------------------------------------------
+
+def _masked_scores(Q, K, q_start, q_end, k_start, k_end, scale, causal):
+    S = (Q[q_start:q_end] @ K[k_start:k_end].T) * scale
+    if causal:
+        q_pos = np.arange(q_start, q_end)[:, None]
+        k_pos = np.arange(k_start, k_end)[None, :]
+        S = np.where(q_pos >= k_pos, S, NEG_INF)
+    return S
+
+
+def blocked_backward(Q, K, V, O, dO, LSE, Br: int, Bc: int, scale: float, causal: bool = False,
+                     blocklocal_rowsum: bool = False):
+    """The two-kernel backward ("9.4 FlashAttention 与 FlashMLA", section
+    9.4.5; the block formulas of "6. FlashAttention 分块逻辑", section 7):
+
+    * pre-pass: D_i = rowsum(dO_i * O_i);
+    * dK/dV: K/V blocks outer, Q blocks inner; per pair recompute
+      S = scale Q_i K_j^T (+ mask) and P = exp(S - LSE_i) from the saved
+      statistic, then dV_j += P^T dO_i, dP = dO_i V_j^T,
+      dS = P * (dP - D_i), dK_j += scale dS^T Q_i;
+    * dQ: Q blocks outer, K/V blocks inner; the same P, dP, dS, then
+      dQ_i += scale dS K_j.
+
+    ``blocklocal_rowsum=True`` replaces D_i by the block-local sum
+    rowsum(dP * P) over the current K/V block, as the first page's block
+    listing writes it.  That equals D_i only when one block holds the whole
+    row; the variant exists so a test can show the difference.
+
+    Single head: Q, O, dO [Nq, d]; K, V [Nk, d]; LSE [Nq] (natural log).
+    Returns (dQ, dK, dV).
+    """
+    Q, K, V, O, dO = (np.asarray(a, dtype=np.float64) for a in (Q, K, V, O, dO))
+    LSE = np.asarray(LSE, dtype=np.float64)
+    Nq, d = Q.shape
+    Nk = K.shape[0]
+    Dvec = (dO * O).sum(axis=1)
+    dQ = np.zeros((Nq, d))
+    dK = np.zeros((Nk, d))
+    dV = np.zeros((Nk, d))
+
+    def grads(q_start, q_end, k_start, k_end):
+        S = _masked_scores(Q, K, q_start, q_end, k_start, k_end, scale, causal)
+        P = np.exp(S - LSE[q_start:q_end, None])
+        dP = dO[q_start:q_end] @ V[k_start:k_end].T
+        if blocklocal_rowsum:
+            Di = (dP * P).sum(axis=1, keepdims=True)
+        else:
+            Di = Dvec[q_start:q_end, None]
+        return P, P * (dP - Di)
+
+    for k_start in range(0, Nk, Bc):                 # dK / dV
+        k_end = min(Nk, k_start + Bc)
+        for q_start in range(0, Nq, Br):
+            q_end = min(Nq, q_start + Br)
+            if causal and _causal_case(q_start, q_end, k_start, k_end) == "skip":
+                continue
+            P, dS = grads(q_start, q_end, k_start, k_end)
+            dV[k_start:k_end] += P.T @ dO[q_start:q_end]
+            dK[k_start:k_end] += scale * (dS.T @ Q[q_start:q_end])
+    for q_start in range(0, Nq, Br):                 # dQ
+        q_end = min(Nq, q_start + Br)
+        for k_start in range(0, Nk, Bc):
+            k_end = min(Nk, k_start + Bc)
+            if causal and _causal_case(q_start, q_end, k_start, k_end) == "skip":
+                continue
+            _, dS = grads(q_start, q_end, k_start, k_end)
+            dQ[q_start:q_end] += scale * (dS @ K[k_start:k_end])
+    return dQ, dK, dV
