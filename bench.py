@@ -36,16 +36,21 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA
 PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector (packed)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 KERNEL_SOURCES = ["io_aware_amd/csrc/fa_prefill.hip", "io_aware_amd/csrc/fa_layout.h",
-                  "io_aware_amd/csrc/fa_decode.hip", "io_aware_amd/csrc/fa_f32.hip"]
+                  "io_aware_amd/csrc/fa_decode.hip", "io_aware_amd/csrc/fa_f32.hip",
+                  "io_aware_amd/csrc/fa_backward.hip", "io_aware_amd/csrc/fa_device.h"]
 
 
 def workload_flops(w) -> float:
-    f = 4.0 * w.B * w.H * w.Nq * w.Nk * w.d
+    # forward: Q K^T and P V (4d per visible pair); backward: Q K^T, dO V^T,
+    # P^T dO, dS K and dS^T Q (10d per visible pair)
+    f = (10.0 if w.backward else 4.0) * w.B * w.H * w.Nq * w.Nk * w.d
     return f / 2 if w.causal else f
 
 
 def workload_bytes(w) -> float:
     es = 4 if w.dtype == "f32" else 2
+    if w.backward:  # read q, k, v, out, dout, lse; write dq, dk, dv
+        return float(es * w.B * w.H * (5 * w.Nq * w.d + 4 * w.Nk * w.d) + 4 * w.B * w.H * w.Nq)
     return float(es * w.B * w.H * (2 * w.Nq * w.d + 2 * w.Nk * w.d) + 4 * w.B * w.H * w.Nq)
 
 
@@ -70,11 +75,35 @@ def measured_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def bwd_cpu_baseline(w, q, k, v, target_s: float):
+    """Time the fp64 backward oracle on whole heads (all query and key rows),
+    growing the number of heads until about ``target_s`` of work."""
+    import numpy as np
+    import oracle
+    import fa_inputs
+    threads = len(os.sched_getaffinity(0))
+    qf, kf, vf = (t.float().numpy() for t in (q, k, v))
+    gf = fa_inputs.make_dout(w.B, w.H, w.Nq, w.d, w.dtype, w.seed).float().numpy()
+    n = 1
+    while True:
+        t0 = time.perf_counter()
+        oracle.attention_bwd(qf, kf, vf, gf, w.scale, w.causal, heads=np.arange(n), threads=threads)
+        dt = time.perf_counter() - t0
+        if dt >= target_s or n >= w.B * w.H:
+            break
+        n = min(w.B * w.H, max(n + 1, int(n * target_s / max(dt, 1e-3) * 1.1)))
+    flops = workload_flops(w) / (w.B * w.H) * n
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "heads 0..%d of %d, all rows, %.1f s, fp64 backward oracle" % (n - 1, w.B * w.H, dt)}
+
+
 def cpu_baseline(w, q, k, v, target_s: float):
     """Time the fp64 oracle on a sample of rows; returns the baseline object."""
     import numpy as np
     import oracle
     import fa_inputs
+    if w.backward:
+        return bwd_cpu_baseline(w, q, k, v, target_s)
     threads = len(os.sched_getaffinity(0))
     qf, kf, vf = (t.float().numpy() for t in (q, k, v))   # exact widening, outside the timing
     total_rows = w.B * w.H * w.Nq
@@ -135,7 +164,15 @@ def run_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s=0.3):
     qd, kd, vd = (t.to(dev).contiguous() for t in (q, k, v))
     out = torch.empty_like(qd)
     lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
-    if w.num_splits:
+    if w.backward:
+        fa.fa_fwd(qd, kd, vd, scale=w.scale, causal=w.causal, out=out, lse=lse)
+        dod = fa_inputs.make_dout(w.B, w.H, w.Nq, w.d, w.dtype, w.seed).to(dev)
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.Nq, w.d), dtype=torch.uint8, device=dev)
+
+        def step():
+            fa.fa_bwd(qd, kd, vd, out, dod, lse, scale=w.scale, causal=w.causal, dq=dq, dk=dk, dv=dv, workspace=ws)
+    elif w.num_splits:
         ws = torch.empty(fa.fa_splitkv_workspace_bytes(w.B, w.H, w.Nq, w.d, w.num_splits), dtype=torch.uint8,
                          device=dev)
 

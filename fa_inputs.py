@@ -39,6 +39,7 @@ class Workload:
     seed: int
     q_sigma: float = 1.0
     num_splits: int = 0          # > 0: run through the explicit split-KV entry point
+    backward: bool = False       # the workload of the backward pass (forward output and LSE, then gradients)
     note: str = field(default="", compare=False)
 
     @property
@@ -67,6 +68,8 @@ WORKLOADS = {
                  q_sigma=8.0),
         Workload("decode_bf16_b16h32_nk8192_d128_split32", 16, 32, 1, 8192, 128, "bf16", False, 1005,
                  num_splits=32),
+        Workload("bwd_causal_bf16_b8h16_n4096_d128", 8, 16, 4096, 4096, 128, "bf16", True, 1008, backward=True,
+                 note="the causal prefill shapes, backward"),
     ]
 }
 
@@ -188,6 +191,16 @@ def make_qkv(B: int, H: int, Nq: int, Nk: int, d: int, dtype, seed: int,
 
 def make_workload(w: Workload):
     return make_qkv(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.seed, w.q_sigma)
+
+
+def make_dout(B: int, H: int, Nq: int, d: int, dtype, seed: int):
+    """The upstream gradient dO [B, H, Nq, d]: standard normal in float32 from
+    its own CPU generator (seed + 500000, so it never repeats q's draws),
+    rounded to ``dtype`` (nearest-even)."""
+    if isinstance(dtype, str):
+        dtype = DTYPES[dtype]
+    g = torch.Generator().manual_seed(int(seed) + 500000)
+    return torch.randn((B, H, Nq, d), generator=g, dtype=torch.float32).to(dtype)
 
 
 def sample_rows(B: int, H: int, Nq: int, count: int, seed: int, tile: int = 64):

@@ -146,6 +146,41 @@ int fa_fwd_paged_decode(const void *q, const void *k_cache, const void *v_cache,
                         int dtype, hipStream_t stream);
 
 /*
+ * fa_bwd_workspace_bytes -- bytes of workspace fa_bwd needs: two float32
+ * values per query row (the statistic LSE*log2(e) and D, see fa_bwd) plus a
+ * padding of 64 rows, rounded up to 256 bytes.  Returns 0 for arguments
+ * outside the accepted ranges.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int d);
+
+/*
+ * fa_bwd -- the backward pass by recomputation ("9.4 FlashAttention 与
+ * FlashMLA" section 9.4.5: a pre-computed D_i = rowsum(dO_i * O_i), one
+ * kernel over K/V blocks for dK and dV, one over Q blocks for dQ; "6.
+ * FlashAttention 分块逻辑" section 7.1 for the formulas):
+ *
+ *     P  = exp(scale * Q K^T [+ mask] - LSE)      (rebuilt per block, never stored)
+ *     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),
+ *     dQ = scale * dS K,  dK = scale * dS^T Q.
+ *
+ * q, k, v, causal and scale must be those of the forward call that produced
+ * ``out`` and ``lse`` (lse is required: [B, H, Nq] float32, natural log).
+ * dout: [B, H, Nq, d], the gradient of the loss with respect to out.
+ * dq: [B, H, Nq, d]; dk, dv: [B, H, Nk, d]; all in ``dtype`` (fp16 or bf16;
+ * fp32 is FA_ERR_UNSUPPORTED), rounded to nearest even from float32
+ * accumulators.  P and dS are rounded to ``dtype`` before their products.
+ * Keys that no query sees get dK = dV = 0.  The result is bit-for-bit
+ * reproducible (no atomics).  workspace: caller-owned device memory of at
+ * least fa_bwd_workspace_bytes(B, H, Nq, d) bytes, 16-byte aligned.  dq, dk,
+ * dv must not overlap each other, an input or the workspace.
+ */
+int fa_bwd(const void *q, const void *k, const void *v, const void *out,
+           const void *dout, const float *lse, void *dq, void *dk, void *dv,
+           int B, int H, int Nq, int Nk, int d, float scale, int causal,
+           int dtype, void *workspace, size_t workspace_bytes,
+           hipStream_t stream);
+
+/*
  * fa_default_num_splits -- chunk count fa_fwd uses for a decode call:
  * ceil(Nk / 256) clamped to [1, 64] (8192 keys -> 32 chunks of 256).
  * Returns 0 if Nk < 1.

@@ -37,6 +37,10 @@ _SIGNATURES = {
                                            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
                                            ctypes.c_int, ctypes.c_void_p]),
+    "fa_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
+    "fa_bwd": (ctypes.c_int, [ctypes.c_void_p] * 9 + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int,
+                                                                           ctypes.c_int, ctypes.c_void_p,
+                                                                           ctypes.c_size_t, ctypes.c_void_p]),
     "fa_default_num_splits": (ctypes.c_int, [ctypes.c_int]),
     "fa_release_workspace": (ctypes.c_int, []),
     "fa_map_workgroup": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -193,6 +197,38 @@ def fa_fwd_paged_decode(q, k_cache, v_cache, block_table, seq_lens, num_splits, 
     return out, lse
 
 
+def fa_bwd_workspace_bytes(B, H, Nq, d) -> int:
+    return int(lib.fa_bwd_workspace_bytes(B, H, Nq, d))
+
+
+def fa_bwd(q, k, v, out, dout, lse, scale=None, causal=False, dq=None, dk=None, dv=None, workspace=None,
+           stream=None):
+    """Gradients (dq, dk, dv) of the forward for the upstream gradient
+    ``dout``, from the forward's ``out`` and ``lse`` ([B, H, Nq] float32).
+    ``workspace`` is a device tensor of at least ``fa_bwd_workspace_bytes``
+    bytes (allocated here if None)."""
+    import torch
+    B, H, Nq, Nk, d = _shapes(q, k, v)
+    for name, t in (("out", out), ("dout", dout)):
+        if tuple(t.shape) != tuple(q.shape) or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous device tensor shaped and typed like q" % name)
+    if tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = fa_bwd_workspace_bytes(B, H, Nq, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                      B, H, Nq, Nk, d, float(scale), 1 if causal else 0, _dtype_code(q), _ptr(workspace), ws_bytes,
+                      _stream_handle(q, stream)), "fa_bwd")
+    return dq, dk, dv
+
+
 def fa_default_num_splits(Nk: int) -> int:
     return int(lib.fa_default_num_splits(Nk))
 
@@ -220,6 +256,6 @@ def fa_version() -> int:
     return int(lib.fa_version())
 
 
-__all__ = ["fa_fwd", "fa_fwd_splitkv", "fa_fwd_paged_decode", "fa_splitkv_workspace_bytes", "fa_default_num_splits",
+__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_paged_decode", "fa_splitkv_workspace_bytes", "fa_default_num_splits",
            "fa_release_workspace", "fa_map_workgroup", "fa_status_string", "fa_last_error", "fa_version",
            "FAError", "FA_F32", "FA_F16", "FA_BF16", "lib", "LIB_PATH"]

@@ -236,6 +236,55 @@ int fa_fwd_paged_decode(const void *q, const void *k_cache, const void *v_cache,
                       "paged decode launch");
 }
 
+size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int d) {
+    if (B < 1 || H < 1 || Nq < 1 || (d != 32 && d != 64 && d != 128)) return 0;
+    if ((int64_t)B * H > INT32_MAX) return 0;
+    return (fa::bwd_stats_bytes(B * H, Nq) + 255) / 256 * 256;
+}
+
+int fa_bwd(const void *q, const void *k, const void *v, const void *out, const void *dout, const float *lse,
+           void *dq, void *dk, void *dv, int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+           void *workspace, size_t ws_bytes, hipStream_t stream) {
+    if (!dout || !lse || !dq || !dk || !dv)
+        return fail(FA_ERR_INVALID_ARG, "dout, lse, dq, dk and dv must be non-null");
+    int st = check_common(q, k, v, out, nullptr, B, H, Nq, Nk, d, scale, dtype);
+    if (st != FA_OK) return st;
+    if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (dtype == FA_F32) return fail(FA_ERR_UNSUPPORTED, "the backward takes fp16 or bf16");
+    if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+        return fail(FA_ERR_UNSUPPORTED, "dout, dq, dk and dv must be 16-byte aligned");
+    if (!aligned(lse, 4)) return fail(FA_ERR_UNSUPPORTED, "lse must be 4-byte aligned");
+    const size_t need = fa_bwd_workspace_bytes(B, H, Nq, d);
+    if (need == 0 || need > (size_t)INT32_MAX)
+        return fail(FA_ERR_UNSUPPORTED, "B*H*Nq is too large for the backward's statistics");
+    const size_t es = element_size(dtype);
+    const size_t bh = (size_t)B * H;
+    const size_t q_bytes = bh * Nq * d * es, kv_bytes = bh * Nk * d * es, lse_bytes = bh * Nq * 4;
+    const void *ins[6] = {q, k, v, out, dout, lse};
+    const size_t in_bytes[6] = {q_bytes, kv_bytes, kv_bytes, q_bytes, q_bytes, lse_bytes};
+    void *outs[3] = {dq, dk, dv};
+    const size_t out_bytes[3] = {q_bytes, kv_bytes, kv_bytes};
+    for (int o = 0; o < 3; ++o) {
+        for (int i = 0; i < 6; ++i)
+            if (overlaps(outs[o], out_bytes[o], ins[i], in_bytes[i]))
+                return fail(FA_ERR_INVALID_ARG, "dq, dk and dv must not overlap an input");
+        for (int p = 0; p < o; ++p)
+            if (overlaps(outs[o], out_bytes[o], outs[p], out_bytes[p]))
+                return fail(FA_ERR_INVALID_ARG, "dq, dk and dv must not overlap each other");
+    }
+    if (!workspace || !aligned(workspace, 16) || ws_bytes < need)
+        return fail(FA_ERR_WORKSPACE, "workspace must be 16-byte aligned and hold fa_bwd_workspace_bytes() = " +
+                                          std::to_string(need) + " bytes");
+    for (int i = 0; i < 6; ++i)
+        if (overlaps(workspace, need, ins[i], in_bytes[i])) return fail(FA_ERR_WORKSPACE, "workspace overlaps an input");
+    for (int o = 0; o < 3; ++o)
+        if (overlaps(workspace, need, outs[o], out_bytes[o]))
+            return fail(FA_ERR_WORKSPACE, "workspace overlaps an output");
+    return hip_status(fa::launch_backward(dtype, d, causal != 0, q, k, v, out, dout, lse, dq, dk, dv, B * H, Nq, Nk,
+                                          scale, workspace, stream),
+                      "backward launch");
+}
+
 int fa_default_num_splits(int Nk) {
     if (Nk < 1) return 0;
     int s = (Nk + 255) / 256;

@@ -49,4 +49,12 @@ hipError_t launch_paged_decode(int dtype, int d, const void *q, const void *k_ca
                                int log2_block, int max_blocks, int num_blocks, float scale_log2, int num_splits,
                                void *workspace, hipStream_t stream);
 
+// Backward (bf16 / fp16, MFMA): the dQ kernel (which also writes the
+// per-query statistics the second kernel reads) then the dK/dV kernel, in
+// stream order.  workspace holds bwd_stats_bytes(BH, Nq) bytes.
+size_t bwd_stats_bytes(int BH, int Nq);
+hipError_t launch_backward(int dtype, int d, bool causal, const void *q, const void *k, const void *v,
+                           const void *out, const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                           int BH, int Nq, int Nk, float scale, void *workspace, hipStream_t stream);
+
 }  // namespace fa

@@ -77,6 +77,19 @@ FA_HD int v_swizzle(int key) {
     return (4 * ((key / R) & 3)) & (CH - 1);
 }
 
+template <int D>
+FA_HD int dual_swizzle(int key) {
+    // a tile read both ways (the backward's Q, dO and K tiles): row-wise as
+    // the K operand (16 consecutive rows, one chunk column) and transposed as
+    // the V operand (4 consecutive rows x an aligned group of 4 chunks).  With
+    // n = key / R, the low bits of n pick the quarter of the bank line a row's
+    // chunk group goes to (4 consecutive rows: 4 quarters), the next bits
+    // rotate chunks within the quarter (16 consecutive rows: 16 positions).
+    constexpr int CH = D / 8, R = 16 / CH, QC = CH / 4;
+    const int n = key / R;
+    return (((n % QC) * 4) ^ ((n / QC) & 3)) & (CH - 1);
+}
+
 // Byte offset of element (key, dim) of a K or V tile in LDS.
 template <int D>
 FA_HD int k_elem_offset(int key, int dim) {
@@ -85,6 +98,11 @@ FA_HD int k_elem_offset(int key, int dim) {
 template <int D>
 FA_HD int v_elem_offset(int key, int dim) {
     return key * (D * 2) + (((dim >> 3) ^ v_swizzle<D>(key)) << 4) + (dim & 7) * 2;
+}
+
+template <int D>
+FA_HD int dual_elem_offset(int key, int dim) {
+    return key * (D * 2) + (((dim >> 3) ^ dual_swizzle<D>(key)) << 4) + (dim & 7) * 2;
 }
 
 // DMA: LDS unit u of a tile (u = 64 * instruction_slot + lane) receives
@@ -101,6 +119,13 @@ FA_HD int v_dma_src_elem(int u) {
     constexpr int CH = D / 8;
     const int key = u / CH;
     return key * D + (((u % CH) ^ v_swizzle<D>(key)) * 8);
+}
+
+template <int D>
+FA_HD int dual_dma_src_elem(int u) {
+    constexpr int CH = D / 8;
+    const int key = u / CH;
+    return key * D + (((u % CH) ^ dual_swizzle<D>(key)) * 8);
 }
 
 // ---------------------------------------------------------------------------
@@ -125,6 +150,20 @@ FA_HD int v_operand_tr_offset(int db, int lane, int ks2, int sh) {
     const int key = 16 * ks2 + 8 * sh + 4 * (G >> 1) + (j >> 2);
     const int dim = 32 * db + 16 * (G & 1) + 4 * (j & 3);
     return v_elem_offset<D>(key, dim);
+}
+
+// The same two reads on a dual-swizzled tile (rows are keys of a K tile, or
+// queries of a Q or dO tile).
+template <int D>
+FA_HD int dual_row_operand_offset(int kb, int l32, int g, int ks) {
+    return dual_elem_offset<D>(32 * kb + l32, 16 * ks + 8 * g);
+}
+template <int D>
+FA_HD int dual_tr_operand_offset(int db, int lane, int ks2, int sh) {
+    const int G = lane >> 4, j = lane & 15;
+    const int key = 16 * ks2 + 8 * sh + 4 * (G >> 1) + (j >> 2);
+    const int dim = 32 * db + 16 * (G & 1) + 4 * (j & 3);
+    return dual_elem_offset<D>(key, dim);
 }
 
 // Model of the transposed read for host checks: the (address owner lane,

@@ -47,50 +47,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_device.h"
 #include "fa_internal.h"
 #include "fa_layout.h"
 
-#define FA_LDS __attribute__((address_space(3)))
-
 namespace fa {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-
-template <typename T>
-struct Mfma;
-
-template <>
-struct Mfma<__bf16> {
-    typedef bf16x8 x8;
-    typedef bf16x4 x4;
-    static __device__ __forceinline__ f32x16 run(x8 a, x8 b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-    }
-};
-
-template <>
-struct Mfma<_Float16> {
-    typedef f16x8 x8;
-    typedef f16x4 x4;
-    static __device__ __forceinline__ f32x16 run(x8 a, x8 b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-    }
-};
-
-template <int N>
-struct Int {
-    static constexpr int value = N;
-};
 
 struct PrefillArgs {
     const void *q;
@@ -109,18 +71,6 @@ struct PrefillArgs {
 // P <= 2^8 (see the online-softmax step of prefill_kernel).
 constexpr float kHeldSumBound = 256.0f;
 constexpr float kLn2 = 0.693147180559945309417f;
-// word 3 of a raw buffer descriptor on gfx9-family parts
-constexpr int kBufferDword3 = 0x00020000;
-
-__device__ __forceinline__ float xor32_max(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ __forceinline__ float xor32_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 template <typename T, int D, bool CAUSAL, int NW, int QW, int BC, int OCC>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC)))

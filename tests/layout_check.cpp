@@ -34,13 +34,21 @@ static int g_fail = 0;
     } while (0)
 
 // LDS element map after DMA: element index (byte / 2) -> source element key*D + dim
-template <int D, int BC, bool IS_V>
+// kind: 0 = K swizzle, 1 = V swizzle, 2 = dual swizzle
+template <int D> int src_of(int kind, int u) {
+    return kind == 0 ? k_dma_src_elem<D>(u) : kind == 1 ? v_dma_src_elem<D>(u) : dual_dma_src_elem<D>(u);
+}
+template <int D> int off_of(int kind, int key, int dim) {
+    return kind == 0 ? k_elem_offset<D>(key, dim) : kind == 1 ? v_elem_offset<D>(key, dim) : dual_elem_offset<D>(key, dim);
+}
+
+template <int D, int BC, int KIND>
 std::vector<int> dma_tile() {
     constexpr int CH = D / 8;
     constexpr int TILE = BC * D * 2;
     std::vector<int> lds(TILE / 2, -1), seen(BC * D, 0);
     for (int u = 0; u < BC * CH; ++u) {
-        const int src = IS_V ? v_dma_src_elem<D>(u) : k_dma_src_elem<D>(u);
+        const int src = src_of<D>(KIND, u);
         CHECK(src >= 0 && src + 8 <= BC * D && src % 8 == 0, "DMA source chunk out of the tile");
         if (src < 0 || src + 8 > BC * D) continue;
         for (int e = 0; e < 8; ++e) {
@@ -51,7 +59,7 @@ std::vector<int> dma_tile() {
     for (int i = 0; i < BC * D; ++i) CHECK(seen[i] == 1, "DMA does not place every element exactly once");
     for (int key = 0; key < BC; ++key)
         for (int dim = 0; dim < D; ++dim) {
-            const int off = IS_V ? v_elem_offset<D>(key, dim) : k_elem_offset<D>(key, dim);
+            const int off = off_of<D>(KIND, key, dim);
             CHECK(off >= 0 && off + 2 <= TILE, "element offset out of the tile");
             if (off >= 0 && off + 2 <= TILE) CHECK(lds[off / 2] == key * D + dim, "element offset disagrees with DMA");
         }
@@ -76,8 +84,8 @@ int bank_degree(const std::vector<std::pair<int, int>> &acc) {
 template <int D, int BC>
 void check_tile() {
     constexpr int TILE = BC * D * 2;
-    std::vector<int> klds = dma_tile<D, BC, false>();
-    std::vector<int> vlds = dma_tile<D, BC, true>();
+    std::vector<int> klds = dma_tile<D, BC, 0>();
+    std::vector<int> vlds = dma_tile<D, BC, 1>();
     int kdeg = 0, vdeg = 0;
 
     for (int kb = 0; kb < BC / 32; ++kb)
@@ -146,6 +154,62 @@ void check_tile() {
     if (D >= 64) CHECK(kdeg == 1 && vdeg == 1, "operand reads conflict under the 64-bank model D=%d BC=%d", D, BC);
 }
 
+// A dual-swizzled tile: both the row read and the transposed read fetch the
+// right elements and are conflict-free (every d).
+template <int D, int BC>
+void check_dual_tile() {
+    constexpr int TILE = BC * D * 2;
+    std::vector<int> lds = dma_tile<D, BC, 2>();
+    int rdeg = 0, tdeg = 0;
+    for (int kb = 0; kb < BC / 32; ++kb)
+        for (int ks = 0; ks < D / 16; ++ks) {
+            std::vector<std::pair<int, int>> phase;
+            for (int lane = 0; lane < 64; ++lane) {
+                const int l32 = lane & 31, g = lane >> 5;
+                const int off = dual_row_operand_offset<D>(kb, l32, g, ks);
+                CHECK(off >= 0 && off + 16 <= TILE && off % 16 == 0, "dual row read out of range");
+                if (off < 0 || off + 16 > TILE) continue;
+                for (int e = 0; e < 8; ++e)
+                    CHECK(lds[off / 2 + e] == (32 * kb + l32) * D + 16 * ks + 8 * g + e, "dual row read wrong D=%d", D);
+                CHECK(off == dual_row_operand_offset<D>(0, l32, g, ks) + 32 * kb * D * 2, "dual row offset not lane + const");
+                phase.push_back({off, 16});
+                if (phase.size() == 16) {
+                    int d = bank_degree(phase);
+                    rdeg = rdeg > d ? rdeg : d;
+                    phase.clear();
+                }
+            }
+        }
+    for (int db = 0; db < D / 32; ++db)
+        for (int ks2 = 0; ks2 < BC / 16; ++ks2)
+            for (int sh = 0; sh < 2; ++sh)
+                for (int G = 0; G < 4; ++G) {
+                    int addr[16];
+                    std::vector<std::pair<int, int>> phase;
+                    for (int j = 0; j < 32; ++j) phase.push_back({dual_tr_operand_offset<D>(db, 16 * (G & 2) + j, ks2, sh), 8});
+                    int d = bank_degree(phase);
+                    tdeg = tdeg > d ? tdeg : d;
+                    for (int j = 0; j < 16; ++j) {
+                        addr[j] = dual_tr_operand_offset<D>(db, 16 * G + j, ks2, sh);
+                        CHECK(addr[j] >= 0 && addr[j] + 8 <= TILE && addr[j] % 8 == 0, "dual tr read out of range");
+                        // the slot half changes the swizzle: one lane part per (db, sh), k-steps add a constant
+                        CHECK(addr[j] == dual_tr_operand_offset<D>(db, 16 * G + j, 0, sh) + 16 * ks2 * D * 2,
+                              "dual tr offset not lane + const");
+                    }
+                    for (int i = 0; i < 16; ++i)
+                        for (int e = 0; e < 4; ++e) {
+                            const int a = addr[tr_src_lane(i, e)];
+                            if (a < 0 || a + 8 > TILE) continue;
+                            const int got = lds[a / 2 + tr_src_elem(i)];
+                            const int lane = 16 * G + i, g = lane >> 5, l32 = lane & 31;
+                            const int want = pv_key(ks2, g, 4 * sh + e) * D + (32 * db + l32);
+                            CHECK(got == want, "dual tr read wrong D=%d BC=%d", D, BC);
+                        }
+                }
+    std::printf("D=%3d BC=%3d: dual tile row-read conflict degree %d, transposed-read %d\n", D, BC, rdeg, tdeg);
+    CHECK(rdeg == 1 && tdeg == 1, "dual tile reads conflict D=%d BC=%d", D, BC);
+}
+
 void check_maps() {
     std::vector<int> seen(32, 0);
     for (int r = 0; r < 16; ++r)
@@ -194,6 +258,11 @@ int main() {
     check_tile<128, 64>();
     check_tile<128, 32>();
     check_tile<128, 128>();
+    check_dual_tile<32, 64>();
+    check_dual_tile<64, 32>();
+    check_dual_tile<64, 64>();
+    check_dual_tile<128, 32>();
+    check_dual_tile<128, 64>();
     check_maps();
     check_workgroups();
     if (g_fail) return 1;

@@ -39,7 +39,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for want in ("fa_fwd", "fa_fwd_splitkv", "fa_fwd_paged_decode", "fa_splitkv_workspace_bytes", "fa_status_string",
+    for want in ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_paged_decode", "fa_splitkv_workspace_bytes", "fa_status_string",
                  "fa_last_error", "fa_release_workspace", "fa_default_num_splits", "fa_map_workgroup"):
         assert want in names
 
@@ -206,3 +206,39 @@ def test_paged_decode_rejects_small_workspace(fa):
     need = fa.fa_splitkv_workspace_bytes(4, 8, 1, 128, 8)
     assert call_paged(fa, ws_bytes=need - 1) == 4
     assert "workspace" in fa.fa_last_error()
+
+
+BQ_, BK_, BV_, BO_, BDO_, BL_, GQ_, GK_, GV_, BW_ = (0x10000000 * i for i in range(12, 22))
+BGOOD = dict(q=BQ_, k=BK_, v=BV_, out=BO_, dout=BDO_, lse=BL_, dq=GQ_, dk=GK_, dv=GV_, B=2, H=4, Nq=100, Nk=120,
+             d=64, scale=0.125, causal=1, dtype=2, ws=BW_)
+
+
+def call_bwd(fa, ws_bytes=None, **over):
+    a = dict(BGOOD)
+    a.update(over)
+    if ws_bytes is None:
+        ws_bytes = fa.fa_bwd_workspace_bytes(a["B"], a["H"], a["Nq"], 64)
+    return fa.lib.fa_bwd(a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"],
+                         a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"], a["dtype"], a["ws"],
+                         ws_bytes, None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), 1), (dict(dout=None), 1), (dict(lse=None), 1), (dict(dq=None), 1), (dict(dk=None), 1),
+    (dict(dv=None), 1), (dict(out=None), 1), (dict(B=0), 1), (dict(Nk=0), 1), (dict(scale=math.inf), 1),
+    (dict(causal=3), 1),
+    (dict(dtype=0), 2), (dict(d=48), 2), (dict(dout=BDO_ + 8), 2), (dict(dq=GQ_ + 8), 2), (dict(lse=BL_ + 2), 2),
+    (dict(dq=BQ_ + 64), 1), (dict(dk=BV_), 1), (dict(dv=BL_), 1), (dict(dv=GK_ + 64), 1), (dict(dk=BDO_), 1),
+    (dict(ws=None), 4), (dict(ws=BW_ + 8), 4), (dict(ws=BO_), 4), (dict(ws=GV_ + 16), 4),
+])
+def test_bwd_rejects_invalid_arguments(fa, over, code):
+    assert call_bwd(fa, **over) == code
+    assert fa.fa_last_error() != ""
+
+
+def test_bwd_workspace_bytes(fa):
+    assert fa.fa_bwd_workspace_bytes(8, 16, 4096, 128) == (8 * 16 * 4096 + 64) * 8
+    assert fa.fa_bwd_workspace_bytes(1, 1, 1, 64) == 768          # 65 rows * 8 bytes = 520, rounded to 256
+    assert fa.fa_bwd_workspace_bytes(1, 1, 1, 48) == 0
+    assert fa.fa_bwd_workspace_bytes(0, 1, 1, 64) == 0
+    assert call_bwd(fa, ws_bytes=fa.fa_bwd_workspace_bytes(2, 4, 100, 64) - 1) == 4

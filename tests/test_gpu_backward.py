@@ -1,0 +1,151 @@
+"""GPU parity of the backward (``fa_bwd``) against the fp64 oracle
+(``oracle.attention_bwd``), through the C ABI.
+
+The forward runs on the GPU first (``fa_fwd``), as a caller would run it, and
+its ``out`` and ``lse`` feed the backward; the oracle computes the exact
+gradients from the same q, k, v and dO.
+
+Tolerance.  The pages state none for gradients.  The bar below comes from the
+arithmetic the kernels do: P and dS are rounded to the 16-bit type before
+their products, accumulation is float32, D is formed from the stored (16-bit)
+O, and outputs are rounded to nearest even.  A CPU emulation of exactly those
+rounding points against the fp64 oracle (causal and non-causal, N up to
+4096, q scaled by 8) gives, per gradient tensor, an element error
+|x - x_ref| / (|x_ref| + rms(x_ref)) of at most 0.067 in bf16 and 0.0037 in
+fp16, and a mean error of at most 2.8e-3 * rms(x_ref) in bf16 and 2e-4 *
+rms(x_ref) in fp16.  The tests allow about twice (bf16) and four times (fp16)
+those figures:
+
+    max |x - x_ref| / (|x_ref| + rms)  <=  0.125 (bf16), 0.016 (fp16)
+    mean |x - x_ref|                   <=  6e-3 * rms (bf16), 1e-3 * rms (fp16)
+"""
+import numpy as np
+import pytest
+import torch
+
+import fa_inputs
+import oracle
+from parity_util import DEV, note, to_dev
+
+pytestmark = pytest.mark.gpu
+
+BWD_TOL = {"bf16": (0.125, 6e-3), "f16": (0.016, 1e-3)}
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import io_aware_amd
+    return io_aware_amd
+
+
+def compare_grad(x, ref, dtype, label):
+    x = x.detach().float().cpu().numpy().astype(np.float64).reshape(ref.shape)
+    assert np.isfinite(x).all(), label + ": non-finite gradient"
+    err = np.abs(x - ref)
+    rms = float(np.sqrt((ref ** 2).mean()))
+    if rms == 0.0:
+        # an exactly-zero gradient (a single key: P = 1, dS = 0) comes out as
+        # float32 rounding noise of dP - D, far below 16-bit resolution
+        assert err.max() <= 1e-4, "%s: %.3e where the gradient is 0" % (label, err.max())
+        return
+    elem = (err / (np.abs(ref) + rms)).max()
+    max_tol, mean_tol = BWD_TOL[dtype]
+    note("%s: rms=%.3e max|d|=%.3e elem=%.3e mean/rms=%.3e" % (label, rms, err.max(), elem, err.mean() / rms))
+    assert elem <= max_tol, "%s: max |d|/(|ref|+rms) %.3e > %.3e" % (label, elem, max_tol)
+    assert err.mean() <= mean_tol * rms, "%s: mean |d| %.3e > %.1e * rms" % (label, err.mean(), mean_tol)
+
+
+def run_bwd(fa, B, H, Nq, Nk, d, dtype, causal, seed, q_sigma=1.0, label=None):
+    label = label or "bwd B%d H%d Nq%d Nk%d d%d %s causal=%d" % (B, H, Nq, Nk, d, dtype, causal)
+    note("case " + label)
+    q, k, v = fa_inputs.make_qkv(B, H, Nq, Nk, d, dtype, seed, q_sigma)
+    g = fa_inputs.make_dout(B, H, Nq, d, dtype, seed)
+    scale = fa_inputs.default_scale(d)
+    qd, kd, vd, gd = to_dev(q, k, v, g)
+    out, lse = fa.fa_fwd(qd, kd, vd, scale=scale, causal=causal)
+    dq, dk, dv = fa.fa_bwd(qd, kd, vd, out, gd, lse, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    ref = oracle.attention_bwd(q, k, v, g, scale, causal)
+    for name, x, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        compare_grad(x, r, dtype, "%s %s" % (label, name))
+    return (q, k, v, g), (dq, dk, dv), ref
+
+
+SHAPES = [(1, 2, 300, 300), (2, 1, 517, 200), (1, 1, 129, 300), (1, 3, 64, 64), (1, 1, 1, 77), (1, 2, 255, 1)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_shapes(fa, dtype, d, causal):
+    for i, (B, H, Nq, Nk) in enumerate(SHAPES):
+        run_bwd(fa, B, H, Nq, Nk, d, dtype, causal, seed=700 + i)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_medium_bf16(fa, causal):
+    run_bwd(fa, 1, 4, 1024, 1024, 128, "bf16", causal, seed=710)
+
+
+def test_large_scores_bf16(fa):
+    run_bwd(fa, 1, 2, 1000, 1000, 128, "bf16", False, seed=711, q_sigma=8.0)
+
+
+def test_keys_no_query_sees_get_zero(fa):
+    # causal with Nk > Nq: keys >= Nq are after every query
+    (q, k, v, g), (dq, dk, dv), _ = run_bwd(fa, 1, 2, 100, 300, 64, "bf16", True, seed=712)
+    assert (dk[:, :, 100:] == 0).all() and (dv[:, :, 100:] == 0).all()
+
+
+def test_full_size_workload_sampled_heads(fa):
+    w = fa_inputs.WORKLOADS["bwd_causal_bf16_b8h16_n4096_d128"]
+    note("case " + w.name)
+    q, k, v = fa_inputs.make_workload(w)
+    g = fa_inputs.make_dout(w.B, w.H, w.Nq, w.d, w.dtype, w.seed)
+    qd, kd, vd, gd = to_dev(q, k, v, g)
+    out, lse = fa.fa_fwd(qd, kd, vd, scale=w.scale, causal=True)
+    dq, dk, dv = fa.fa_bwd(qd, kd, vd, out, gd, lse, scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
+    heads = np.array([0, 77, 127])
+    rows = np.unique(np.r_[0, 1, 31, 32, 127, 128, 2047, 2048, 4094, 4095,
+                           np.random.default_rng(5).integers(0, 4096, 40)])
+    ref = oracle.attention_bwd(q, k, v, g, w.scale, True, heads=heads, q_idx=rows, k_idx=rows)
+    hs, rs = torch.from_numpy(heads), torch.from_numpy(rows)
+    for name, x, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        sel = x.reshape(w.B * w.H, w.Nq, w.d).cpu()[hs][:, rs]
+        compare_grad(sel, r, w.dtype, "%s %s" % (w.name, name))
+
+
+def test_bitwise_deterministic(fa):
+    q, k, v = fa_inputs.make_qkv(2, 2, 700, 700, 128, "bf16", 720)
+    g = fa_inputs.make_dout(2, 2, 700, 128, "bf16", 720)
+    qd, kd, vd, gd = to_dev(q, k, v, g)
+    out, lse = fa.fa_fwd(qd, kd, vd, causal=True)
+    a = fa.fa_bwd(qd, kd, vd, out, gd, lse, causal=True)
+    b = fa.fa_bwd(qd, kd, vd, out, gd, lse, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_guard_bands_untouched(fa):
+    B, H, Nq, Nk, d = 1, 2, 333, 250, 64
+    q, k, v = fa_inputs.make_qkv(B, H, Nq, Nk, d, "f16", 730)
+    g = fa_inputs.make_dout(B, H, Nq, d, "f16", 730)
+    qd, kd, vd, gd = to_dev(q, k, v, g)
+    out, lse = fa.fa_fwd(qd, kd, vd, causal=False)
+    pad = 4096
+    bufs, views = [], []
+    for n, shape in ((B * H * Nq * d, (B, H, Nq, d)), (B * H * Nk * d, (B, H, Nk, d)), (B * H * Nk * d, (B, H, Nk, d))):
+        buf = torch.full((n + 2 * pad,), 7.0, dtype=torch.float16, device=DEV)
+        bufs.append((buf, n))
+        views.append(buf[pad:pad + n].view(*shape))
+    fa.fa_bwd(qd, kd, vd, out, gd, lse, causal=False, dq=views[0], dk=views[1], dv=views[2])
+    torch.cuda.synchronize()
+    for buf, n in bufs:
+        assert (buf[:pad].float() == 7.0).all() and (buf[pad + n:].float() == 7.0).all()
+    ref = oracle.attention_bwd(q, k, v, g, fa_inputs.default_scale(d), False)
+    for name, x, r in zip(("dQ", "dK", "dV"), views, ref):
+        compare_grad(x, r, "f16", "guard bands " + name)
