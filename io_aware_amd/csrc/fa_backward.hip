@@ -20,19 +20,22 @@
 //    gathered by the transposing LDS read.  The kernel also forms D_i from
 //    its O and dO rows and writes (LSE_i log2 e, D_i) for the second kernel.
 //  * dK/dV kernel (K/V blocks outer, Q blocks inner).  A workgroup of 4
-//    waves owns 128 keys; each wave keeps the K and V fragments of its 32
-//    keys and its dK, dV accumulators in registers; Q and dO tiles and their
-//    statistics stream through LDS.  Per tile S = Q K^T and dP = dO V^T (each
-//    lane's registers belong to one key), P and dS in registers, then
-//    dV^T += dO^T P and dK^T += Q^T dS with the dO^T and Q^T operands
-//    gathered by the transposing LDS read.
+//    waves owns 128 keys; each wave keeps the K fragments of its 32 keys and
+//    its dK, dV accumulators in registers, and reads its V rows from LDS
+//    (staged once), which keeps the kernel within two waves per SIMD; Q and
+//    dO tiles and their statistics stream through LDS.  Per tile S = Q K^T
+//    and dP = dO V^T (each lane's registers belong to one key), P and dS in
+//    registers, then dV^T += dO^T P and dK^T += Q^T dS with the dO^T and Q^T
+//    operands gathered by the transposing LDS read.
 //
 // Tiles read both row-wise and transposed (K in the dQ kernel, Q and dO in
 // the dK/dV kernel) use the dual XOR swizzle of fa_layout.h, which keeps both
 // reads free of LDS bank conflicts.  Masked entries (causal, ragged tails)
-// are set to P = dS = 0 by selection, so stale or non-finite values never
-// reach an accumulator; tail rows are fetched from the last valid row so no
-// load leaves its tensor.
+// get S = -inf, so P = 0 and, since dP and the statistics are finite,
+// dS = 0; tail rows are fetched from the last valid row so no load leaves its
+// tensor, and the statistics padding after the last head is zeroed.
+#include <cstdlib>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 #include "fa_layout.h"
@@ -41,6 +44,7 @@ namespace fa {
 namespace {
 
 constexpr float kLog2eF = 1.4426950408889634074f;
+constexpr int kStatsPad = 64;  // statistics rows of padding after the last head (one dK/dV query tile)
 
 struct BwdArgs {
     const void *q;
@@ -178,6 +182,9 @@ void bwd_dq_kernel(BwdArgs a) {
     const float Di = xor32_sum(dpart);
     const float lse2 = row_ok ? a.lse[(size_t)bh * Nq + row] * kLog2eF : 0.0f;
     if (row_ok && g == 0) a.stats[(size_t)bh * Nq + row] = f32x2{lse2, Di};
+    // the padding after the last head is read (then masked) by the dK/dV
+    // kernel's last tiles: keep it finite
+    if (blockIdx.x == 0 && tid < kStatsPad) a.stats[(size_t)a.BH * Nq + tid] = f32x2{0.0f, 0.0f};
 
     f32x16 dqacc[DB];
 #pragma unroll
@@ -212,8 +219,19 @@ void bwd_dq_kernel(BwdArgs a) {
                 s[kb] = M::run(kf, qf[ks], s[kb]);
                 dp[kb] = M::run(vf, dof[ks], dp[kb]);
             }
-        // ---- dS^T = P^T (dP^T - D), P^T = exp2(c s - LSE log2 e) -------------------
+        // ---- mask: ragged key tail and the causal diagonal (P = exp2(-inf) = 0;
+        // dP is finite, so dS = 0 there too) ---------------------------------------
         const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > q0w);
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + 32 * kb + layout::acc_row(r, g);
+                    if (key >= Nk || (CAUSAL && key > row)) s[kb][r] = -__builtin_inff();
+                }
+        }
+        // ---- dS^T = P^T (dP^T - D), P^T = exp2(c s - LSE log2 e) -------------------
         x8 dsf[KS2];
 #pragma unroll
         for (int ks2 = 0; ks2 < KS2; ++ks2) {
@@ -223,12 +241,7 @@ void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][h + e], c, -lse2));
-                float ds = p * (dp[kb][h + e] - Di);
-                if (need_mask) {
-                    const int key = k0 + 32 * kb + layout::acc_row(h + e, g);
-                    if (key >= Nk || (CAUSAL && key > row)) ds = 0.0f;
-                }
-                t[e] = ds;
+                t[e] = p * (dp[kb][h + e] - Di);
             }
             dsf[ks2] = __builtin_convertvector(t, x8);
         }
@@ -282,7 +295,7 @@ void bwd_dq_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dK and dV
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool CAUSAL, int NW, int BQ, int OCC>
+template <typename T, int D, bool CAUSAL, int NW, int BQ, int OCC, bool VLDS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC)))
 void bwd_dkdv_kernel(BwdArgs a) {
     using M = Mfma<T>;
@@ -307,8 +320,14 @@ void bwd_dkdv_kernel(BwdArgs a) {
     static_assert(UNITS % NT == 0, "a tile must split evenly over the workgroup");
     static_assert(SUNITS <= 64 && BQ * 8 <= 1024, "statistics of a tile: one wave, one slot");
     static_assert(2 * STAGE_BYTES <= 65536, "stage offsets must fit a 16-bit LDS immediate");
+    // VLDS: the workgroup's V rows sit in LDS (read per tile) instead of
+    // registers, which frees 4*D/8 registers per lane for a second wave per SIMD
+    constexpr int VT_OFF = 2 * STAGE_BYTES;
+    constexpr int VT_BYTES = VLDS ? BK * ROW : 0;
+    constexpr int VUNITS = BK * CH;
+    static_assert(!VLDS || VUNITS % NT == 0, "the V rows must split evenly over the workgroup");
 
-    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES + VT_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -384,17 +403,19 @@ void bwd_dkdv_kernel(BwdArgs a) {
     // the last key; their gradients are not stored.
     const int key = k0w + l32;
     const int key_c = key < Nk ? key : Nk - 1;
-    x8 kf[KS], vf[KS];
+    x8 kf[KS], vf[VLDS ? 1 : KS];
+    int voff[KS];
     {
         const T *kp = static_cast<const T *>(a.k) + ((size_t)bh * Nk + key_c) * D;
         const T *vp = static_cast<const T *>(a.v) + ((size_t)bh * Nk + key_c) * D;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             kf[ks] = __builtin_bit_cast(x8, *reinterpret_cast<const u32x4 *>(kp + 16 * ks + 8 * g));
-            vf[ks] = __builtin_bit_cast(x8, *reinterpret_cast<const u32x4 *>(vp + 16 * ks + 8 * g));
+            if constexpr (!VLDS)
+                vf[ks] = __builtin_bit_cast(x8, *reinterpret_cast<const u32x4 *>(vp + 16 * ks + 8 * g));
+            voff[ks] = VT_OFF + layout::k_operand_offset<D>(wave, l32, g, ks);
         }
     }
-
     f32x16 dkacc[DB], dvacc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -403,6 +424,23 @@ void bwd_dkdv_kernel(BwdArgs a) {
             dkacc[db][r] = 0.0f;
             dvacc[db][r] = 0.0f;
         }
+
+    auto issue_v_rows = [&]() {
+        // the workgroup's BK V rows, K-style swizzle (read row-wise only);
+        // rows past the end repeat the last key
+        const T *vhead = static_cast<const T *>(a.v) + (size_t)bh * Nk * D;
+        const __amdgpu_buffer_rsrc_t rsrc_v = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<T *>(vhead), (short)0, (int)((uint32_t)Nk * ROW), kBufferDword3);
+#pragma unroll
+        for (int n = 0; n < VUNITS / NT; ++n) {
+            const int u = (n * NW + wave) * 64 + lane;
+            uint32_t o = (uint32_t)layout::k_dma_src_elem<D>(u) * 2;
+            const int over = k0 + u / CH - (Nk - 1);
+            if (over > 0) o -= (uint32_t)over * ROW;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_v, (FA_LDS void *)(smem + VT_OFF + (n * NW + wave) * 1024),
+                                                     16, o, (uint32_t)k0 * ROW, 0, 0);
+        }
+    };
 
     // query tiles: under the mask only queries >= k0 see a key of the block
     const int q_begin = CAUSAL ? (k0 / BQ) * BQ : 0;
@@ -431,12 +469,28 @@ void bwd_dkdv_kernel(BwdArgs a) {
                 const x8 da = __builtin_bit_cast(
                     x8, *reinterpret_cast<const u32x4 *>(smem + DOOFF + qb * 32 * ROW + qoff[ks]));
                 s[qb] = M::run(qa, kf[ks], s[qb]);
-                dp[qb] = M::run(da, vf[ks], dp[qb]);
+                if constexpr (VLDS) {
+                    const x8 vr = __builtin_bit_cast(x8, *reinterpret_cast<const u32x4 *>(smem + voff[ks]));
+                    dp[qb] = M::run(da, vr, dp[qb]);
+                } else {
+                    dp[qb] = M::run(da, vf[ks], dp[qb]);
+                }
             }
-        // ---- P = exp2(c s - LSE log2 e), dS = P (dP - D) ------------------------
+        // ---- mask: ragged query tail and the causal diagonal (P = exp2(-inf) =
+        // 0; dP and the tile's statistics are finite, so dS = 0 there too) ----------
         // register r of query block qb is query qt + 32*qb + acc_row(r, g);
         // registers 4*rg .. 4*rg+3 are four consecutive queries
         const bool need_mask = (qt + BQ > Nq) || (CAUSAL && qt < k0w + KW - 1);
+        if (need_mask) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int query = qt + 32 * qb + layout::acc_row(r, g);
+                    if (query >= Nq || (CAUSAL && key > query)) s[qb][r] = -__builtin_inff();
+                }
+        }
+        // ---- P = exp2(c s - LSE log2 e), dS = P (dP - D) ------------------------
         x8 pf[KS2], dsf[KS2];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
@@ -451,17 +505,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * rg + e;
-                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], c, -lse2[e]));
-                    float ds = p * (dp[qb][r] - dd[e]);
-                    if (need_mask) {
-                        const int query = qt + qi + e;
-                        if (query >= Nq || (CAUSAL && key > query)) {
-                            p = 0.0f;
-                            ds = 0.0f;
-                        }
-                    }
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], c, -lse2[e]));
                     tp[r >> 3][r & 7] = p;
-                    td[r >> 3][r & 7] = ds;
+                    td[r >> 3][r & 7] = p * (dp[qb][r] - dd[e]);
                 }
             }
             pf[2 * qb] = __builtin_convertvector(tp[0], x8);
@@ -499,6 +545,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     };
 
     if (nt > 0) {
+        if constexpr (VLDS) issue_v_rows();
         issue_tile(q_begin, 0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -531,6 +578,13 @@ void bwd_dkdv_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // Launch
 // ---------------------------------------------------------------------------
+// dK/dV variant: 0 (default) V rows in LDS, two waves per SIMD; 1 V in
+// registers, one wave per SIMD.  FA_BWD_DKDV selects one for sweeps.
+int bwd_dkdv_variant() {
+    const char *env = std::getenv("FA_BWD_DKDV");
+    return (env && env[0] == '1' && env[1] == '\0') ? 1 : 0;
+}
+
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_bwd_typed(BwdArgs a, hipStream_t stream) {
     constexpr int NW = 4;
@@ -546,8 +600,12 @@ hipError_t launch_bwd_typed(BwdArgs a, hipStream_t stream) {
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     a.T = tk;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, NW, BQ, 1>), dim3((unsigned)nk), dim3(NW * 64), 0, stream,
-                       a);
+    if (bwd_dkdv_variant() == 1)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, NW, BQ, 1, false>), dim3((unsigned)nk), dim3(NW * 64), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, NW, BQ, 2, true>), dim3((unsigned)nk), dim3(NW * 64), 0,
+                           stream, a);
     return hipGetLastError();
 }
 
@@ -568,7 +626,7 @@ hipError_t launch_bwd_d(int d, bool causal, const BwdArgs &a, hipStream_t stream
 
 size_t bwd_stats_bytes(int BH, int Nq) {
     // (LSE log2 e, D) per query, plus one tile of padding read past the last head
-    return ((size_t)BH * Nq + 64) * 8;
+    return ((size_t)BH * Nq + kStatsPad) * 8;
 }
 
 hipError_t launch_backward(int dtype, int d, bool causal, const void *q, const void *k, const void *v,

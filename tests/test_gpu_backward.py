@@ -118,6 +118,15 @@ def test_full_size_workload_sampled_heads(fa):
         compare_grad(sel, r, w.dtype, "%s %s" % (w.name, name))
 
 
+@pytest.mark.parametrize("variant", ["0", "1"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_every_dkdv_variant(fa, variant, causal, monkeypatch):
+    monkeypatch.setenv("FA_BWD_DKDV", variant)
+    for d, dtype in ((128, "bf16"), (64, "f16"), (32, "bf16")):
+        run_bwd(fa, 1, 2, 333, 300, d, dtype, causal, seed=740 + d,
+                label="bwd variant %s d%d %s causal=%d" % (variant, d, dtype, causal))
+
+
 def test_bitwise_deterministic(fa):
     q, k, v = fa_inputs.make_qkv(2, 2, 700, 700, 128, "bf16", 720)
     g = fa_inputs.make_dout(2, 2, 700, 128, "bf16", 720)
