@@ -170,6 +170,69 @@ def make_paged(w: PagedWorkload):
     return q.to(w.torch_dtype), k.to(w.torch_dtype), v.to(w.torch_dtype), table, seq_lens
 
 
+@dataclass(frozen=True)
+class VarlenWorkload:
+    """A batch of packed sequences of different lengths: q [total_q, H, d],
+    k and v [total_k, H, d], cumulative offsets [S + 1]."""
+    name: str
+    S: int
+    H: int
+    d: int
+    dtype: str
+    causal: bool
+    seed: int
+    min_len: int
+    max_len: int
+    edge: bool = False           # put the edge lengths first (see make_varlen)
+    same_kv: bool = True         # key lengths equal query lengths (self-attention)
+    note: str = field(default="", compare=False)
+
+    @property
+    def scale(self) -> float:
+        return default_scale(self.d)
+
+    @property
+    def torch_dtype(self):
+        return DTYPES[self.dtype]
+
+
+VARLEN_WORKLOADS = {
+    w.name: w for w in [
+        VarlenWorkload("varlen_causal_bf16_s16h16_len256to8192_d128", 16, 16, 128, "bf16", True, 1009, 256, 8192,
+                       note="lengths uniform in [256, 8192]: a mixed prefill batch"),
+        VarlenWorkload("varlen_mixed_f16_s9h4_len0to700_d64", 9, 4, 64, "f16", True, 1010, 0, 700, edge=True,
+                       same_kv=False),
+    ]
+}
+
+
+def make_varlen(w: VarlenWorkload):
+    """(q, k, v, cu_seqlens_q, cu_seqlens_k) on the CPU.
+
+    Recipe: a CPU generator seeded with ``w.seed`` draws the query lengths
+    (uniform in [min_len, max_len]; with ``edge`` the lengths 0, 1, 127, 128,
+    129 and max_len come first), then, unless ``same_kv``, the key lengths
+    the same way, then q [total_q, H, d], k and v [total_k, H, d], standard
+    normal in float32, rounded to the dtype (nearest-even).  Offsets are
+    int32 cumulative sums starting at 0.
+    """
+    g = torch.Generator().manual_seed(int(w.seed))
+
+    def lengths():
+        x = torch.randint(w.min_len, w.max_len + 1, (w.S,), generator=g).tolist()
+        if w.edge:
+            x = ([0, 1, 127, 128, 129, w.max_len] + x)[:w.S]
+        return x
+    lq = lengths()
+    lk = lq if w.same_kv else lengths()
+    cq = torch.tensor([0] + lq, dtype=torch.int64).cumsum(0).to(torch.int32)
+    ck = torch.tensor([0] + lk, dtype=torch.int64).cumsum(0).to(torch.int32)
+    q = torch.randn((int(cq[-1]), w.H, w.d), generator=g, dtype=torch.float32)
+    k = torch.randn((int(ck[-1]), w.H, w.d), generator=g, dtype=torch.float32)
+    v = torch.randn((int(ck[-1]), w.H, w.d), generator=g, dtype=torch.float32)
+    return q.to(w.torch_dtype), k.to(w.torch_dtype), v.to(w.torch_dtype), cq, ck
+
+
 # The fp16 shapes of the Triton page's own test (seed 42, 2-D per-head inputs,
 # seqlen_q x seqlen_k x head_dim), run here as B = H = 1.
 TRITON_PAGE_SHAPES = [(256, 256, 64), (128, 256, 64), (64, 64, 32)]

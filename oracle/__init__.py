@@ -24,6 +24,10 @@ Two parts:
   a sequence's block table maps (unallocated blocks dropped) are gathered in
   logical order into a contiguous K/V, which ``attention`` then takes.
   Source: "6. FlashAttention 分块逻辑" section 12.
+* ``varlen_attention`` -- attention over a batch of packed sequences of
+  different lengths: each sequence, cut out of the packed tensors by its
+  cumulative offsets, goes through ``attention`` on its own.  Source: "9.4
+  FlashAttention 与 FlashMLA" section 9.4.6 (variable-length batches).
 * ``oracle.algorithms`` -- the pages' algorithms (one-pass online softmax,
   blocked forward with deferred or per-step normalisation, split-KV partials
   and their merge) in numpy fp64.  They exist to pin ``attention`` and each
@@ -244,3 +248,40 @@ def attention_bwd(q, k, v, dout, scale: float, causal: bool, heads=None, q_idx=N
         dq, dk, dv = dq.reshape(B, H, Nq, d), dk.reshape(B, H, Nk, d), dv.reshape(B, H, Nk, d)
         delta = delta.reshape(B, H, Nq)
     return (dq, dk, dv, delta) if with_delta else (dq, dk, dv)
+
+
+def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: bool, seqs=None, threads: int = 0):
+    """Exact attention over packed variable-length sequences, in fp64.
+
+    q: [total_q, H, d]; k, v: [total_k, H, d] (token-major, heads inside);
+    cu_seqlens_q, cu_seqlens_k: [S + 1] non-decreasing offsets starting at 0.
+    Sequence s is q[cu_q[s]:cu_q[s+1]] attending to k, v[cu_k[s]:cu_k[s+1]]
+    with ``attention`` (causal: top-left within the sequence).  A query with
+    no key gets O = 0 and LSE = -inf.  ``seqs`` restricts the work to some
+    sequences (the other rows of the result stay NaN).
+
+    Returns (out [total_q, H, d], lse [H, total_q]), float64.
+    """
+    qa, ka, va = _as_f32(q), _as_f32(k), _as_f32(v)
+    cq = np.asarray(cu_seqlens_q.cpu() if hasattr(cu_seqlens_q, "cpu") else cu_seqlens_q, dtype=np.int64)
+    ck = np.asarray(cu_seqlens_k.cpu() if hasattr(cu_seqlens_k, "cpu") else cu_seqlens_k, dtype=np.int64)
+    total_q, H, d = qa.shape
+    S = cq.size - 1
+    out = np.full((total_q, H, d), np.nan)
+    lse = np.full((H, total_q), np.nan)
+    for s in (range(S) if seqs is None else seqs):
+        a, b = int(cq[s]), int(cq[s + 1])
+        ka_, kb_ = int(ck[s]), int(ck[s + 1])
+        if b <= a:
+            continue
+        if kb_ <= ka_:
+            out[a:b] = 0.0
+            lse[:, a:b] = -np.inf
+            continue
+        qs = np.ascontiguousarray(qa[a:b].transpose(1, 0, 2))[None]      # [1, H, n, d]
+        ks = np.ascontiguousarray(ka[ka_:kb_].transpose(1, 0, 2))[None]
+        vs = np.ascontiguousarray(va[ka_:kb_].transpose(1, 0, 2))[None]
+        o, l = attention(qs, ks, vs, scale, causal, threads=threads)
+        out[a:b] = o[0].transpose(1, 0, 2)
+        lse[:, a:b] = l[0]
+    return out, lse
