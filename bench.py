@@ -158,6 +158,8 @@ def run_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s=0.3):
 
     if name in fa_inputs.PAGED_WORKLOADS:
         return run_paged_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s)
+    if name in fa_inputs.VARLEN_WORKLOADS:
+        return run_varlen_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s)
     w = fa_inputs.WORKLOADS[name]
     q, k, v = fa_inputs.make_workload(w)
     dev = torch.device("cuda:0")
@@ -275,6 +277,75 @@ def run_paged_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s):
     return rec
 
 
+def varlen_pairs(w, lq, lk):
+    """Visible (query, key) pairs per head of a packed batch."""
+    total = 0
+    for nq, nk in zip(lq, lk):
+        if w.causal:  # top-left: query i sees min(i + 1, nk) keys
+            full = min(nq, nk)
+            total += full * (full + 1) // 2 + max(0, nq - nk) * nk
+        else:
+            total += nq * nk
+    return total
+
+
+def run_varlen_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s):
+    import numpy as np
+    import torch
+    import fa_inputs
+    import io_aware_amd as fa
+
+    w = fa_inputs.VARLEN_WORKLOADS[name]
+    q, k, v, cq, ck = fa_inputs.make_varlen(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, cqd, ckd = (t.to(dev).contiguous() for t in (q, k, v, cq, ck))
+    out = torch.empty_like(qd)
+    lse = torch.empty((w.H, qd.shape[0]), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.fa_varlen_workspace_bytes(w.S, qd.shape[0]), dtype=torch.uint8, device=dev)
+
+    def step():
+        fa.fa_fwd_varlen(qd, kd, vd, cqd, ckd, scale=w.scale, causal=w.causal, out=out, lse=lse, workspace=ws)
+
+    ms_per_step, kernel_ms = time_steps(step, steps, warmup, prewarm_s)
+    lq = (cq[1:] - cq[:-1]).tolist()
+    lk = (ck[1:] - ck[:-1]).tolist()
+    flops = 4.0 * w.d * w.H * varlen_pairs(w, lq, lk)
+    nbytes = float(2 * w.H * w.d * (2 * sum(lq) + 2 * sum(lk)) + 4 * w.H * sum(lq))
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    rec = {
+        "metric": "attention fwd TFLOP/s (and % of MI355X bf16 MFMA/HBM roofline) per config",
+        "value": flops / (ms_per_step * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, "prewarm_s": prewarm_s,
+        "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded randn, seeded length mix)",
+        "config": {"workload": name, "S": w.S, "H": w.H, "d": w.d, "causal": w.causal, "dtype": w.dtype,
+                   "seq_lens": lq, "total_q": sum(lq), "flop_per_step": flops,
+                   "algorithmic_bytes_per_step": nbytes},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(name)},
+    }
+    if with_cpu:
+        import oracle
+        threads = len(os.sched_getaffinity(0))
+        # the shortest sequences first until about cpu_target_s of oracle work
+        order = list(np.argsort(lq))
+        qf, kf, vf = (t.float() for t in (q, k, v))
+        done, t_total, pairs = [], 0.0, 0
+        for sidx in order:
+            t0 = time.perf_counter()
+            oracle.varlen_attention(qf, kf, vf, cq, ck, w.scale, w.causal, seqs=[int(sidx)], threads=threads)
+            t_total += time.perf_counter() - t0
+            done.append(int(sidx))
+            pairs += varlen_pairs(w, [lq[sidx]], [lk[sidx]])
+            if t_total >= cpu_target_s:
+                break
+        rec["cpu_baseline"] = {"value": 4.0 * w.d * w.H * pairs / t_total / 1e12, "unit": "TFLOP/s",
+                               "cores": threads, "kind": "oracle",
+                               "sample": "%d of %d sequences, shortest first (lengths %s), %.1f s, fp64 oracle"
+                                         % (len(done), w.S, [lq[i] for i in done], t_total)}
+    return rec
+
+
 def copy_probe(nbytes: int, steps: int) -> int:
     """Plain copies of a known size: each reads and writes ``nbytes`` once."""
     import torch
@@ -312,8 +383,8 @@ def main():
     if args.copy_bytes:
         return copy_probe(args.copy_bytes, args.steps)
     import fa_inputs
-    names = (list(fa_inputs.WORKLOADS) + list(fa_inputs.PAGED_WORKLOADS) if args.workload == "all"
-             else [args.workload])
+    names = (list(fa_inputs.WORKLOADS) + list(fa_inputs.PAGED_WORKLOADS) + list(fa_inputs.VARLEN_WORKLOADS)
+             if args.workload == "all" else [args.workload])
     for i, name in enumerate(names):
         rec = run_workload(name, args.steps, args.warmup,
                            with_cpu=(not args.no_cpu_baseline) and (i == 0 or args.workload != "all"),

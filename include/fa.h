@@ -146,6 +146,39 @@ int fa_fwd_paged_decode(const void *q, const void *k_cache, const void *v_cache,
                         int dtype, hipStream_t stream);
 
 /*
+ * fa_varlen_workspace_bytes -- bytes of workspace fa_fwd_varlen needs for
+ * its tile list: 4 * (2 + 2 * (ceil(total_q / 128) + num_seqs)), rounded up
+ * to 256.  Returns 0 for arguments outside the accepted ranges.
+ */
+size_t fa_varlen_workspace_bytes(int num_seqs, int total_q);
+
+/*
+ * fa_fwd_varlen -- the forward over a batch of packed sequences of different
+ * lengths ("9.4 FlashAttention 与 FlashMLA" section 9.4.6: the work of each
+ * workgroup is fixed before the attention kernel starts, and sequences of
+ * unequal length are cut into equal tiles for load balance).
+ *
+ * q: [total_q, H, d]; k, v: [total_k, H, d]; out: [total_q, H, d] (token-
+ * major, d fastest), element type ``dtype`` (fp16 or bf16).  lse:
+ * [H, total_q] float32 or NULL.  cu_seqlens_q, cu_seqlens_k: device int32
+ * [num_seqs + 1] offsets; sequence s is rows [cu_seqlens_q[s],
+ * cu_seqlens_q[s+1]) of q attending to rows [cu_seqlens_k[s],
+ * cu_seqlens_k[s+1]) of k and v, with the causal mask (if set) top-left
+ * within the sequence.  Offsets must start at 0 and not decrease; on the
+ * device each sequence's bounds are clamped into [0, total] and the tile
+ * list into its bound, so inconsistent offsets give wrong rows, never an
+ * access outside the tensors or the workspace.  A query with no key gets O = 0 and
+ * LSE = -inf.  1 <= num_seqs <= 8192.  A schedule kernel writes the tile
+ * list into ``workspace`` (at least fa_varlen_workspace_bytes(num_seqs,
+ * total_q) bytes, 16-byte aligned), then the attention kernel runs over it.
+ */
+int fa_fwd_varlen(const void *q, const void *k, const void *v, void *out,
+                  float *lse, const int *cu_seqlens_q, const int *cu_seqlens_k,
+                  int num_seqs, int total_q, int total_k, int H, int d,
+                  float scale, int causal, int dtype, void *workspace,
+                  size_t workspace_bytes, hipStream_t stream);
+
+/*
  * fa_bwd_workspace_bytes -- bytes of workspace fa_bwd needs: two float32
  * values per query row (the statistic LSE*log2(e) and D, see fa_bwd) plus a
  * padding of 64 rows, rounded up to 256 bytes.  Returns 0 for arguments

@@ -37,6 +37,11 @@ _SIGNATURES = {
                                            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
                                            ctypes.c_int, ctypes.c_void_p]),
+    "fa_varlen_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 2),
+    "fa_fwd_varlen": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int,
+                                                                                  ctypes.c_int, ctypes.c_void_p,
+                                                                                  ctypes.c_size_t,
+                                                                                  ctypes.c_void_p]),
     "fa_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
     "fa_bwd": (ctypes.c_int, [ctypes.c_void_p] * 9 + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int,
                                                                            ctypes.c_int, ctypes.c_void_p,
@@ -197,6 +202,42 @@ def fa_fwd_paged_decode(q, k_cache, v_cache, block_table, seq_lens, num_splits, 
     return out, lse
 
 
+def fa_varlen_workspace_bytes(num_seqs, total_q) -> int:
+    return int(lib.fa_varlen_workspace_bytes(num_seqs, total_q))
+
+
+def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale=None, causal=False, out=None, lse=None,
+                  return_lse=True, workspace=None, stream=None):
+    """Forward over packed variable-length sequences: q [total_q, H, d],
+    k and v [total_k, H, d], cu_seqlens_* int32 [S + 1] device offsets.
+    Returns (out [total_q, H, d], lse [H, total_q])."""
+    import torch
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or q.shape[1:] != k.shape[1:] or k.shape != v.shape:
+        raise ValueError("q must be [total_q, H, d] and k, v [total_k, H, d]")
+    total_q, H, d = q.shape
+    total_k = k.shape[0]
+    for name, t in (("q", q), ("k", k), ("v", v), ("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous device tensor" % name)
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32 or \
+            cu_seqlens_q.dim() != 1 or cu_seqlens_q.shape != cu_seqlens_k.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must be int32 [S + 1]")
+    S = cu_seqlens_q.shape[0] - 1
+    out = torch.empty_like(q) if out is None else out
+    if lse is None and return_lse:
+        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = fa_varlen_workspace_bytes(S, total_q)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
+                             _ptr(cu_seqlens_k), S, total_q, total_k, H, d, float(scale), 1 if causal else 0,
+                             _dtype_code(q), _ptr(workspace), ws_bytes, _stream_handle(q, stream)), "fa_fwd_varlen")
+    return out, lse
+
+
 def fa_bwd_workspace_bytes(B, H, Nq, d) -> int:
     return int(lib.fa_bwd_workspace_bytes(B, H, Nq, d))
 
@@ -256,6 +297,6 @@ def fa_version() -> int:
     return int(lib.fa_version())
 
 
-__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_paged_decode", "fa_splitkv_workspace_bytes", "fa_default_num_splits",
+__all__ = ["fa_fwd", "fa_fwd_varlen", "fa_varlen_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_paged_decode", "fa_splitkv_workspace_bytes", "fa_default_num_splits",
            "fa_release_workspace", "fa_map_workgroup", "fa_status_string", "fa_last_error", "fa_version",
            "FAError", "FA_F32", "FA_F16", "FA_BF16", "lib", "LIB_PATH"]

@@ -285,6 +285,60 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *out, const v
                       "backward launch");
 }
 
+size_t fa_varlen_workspace_bytes(int num_seqs, int total_q) {
+    if (num_seqs < 1 || num_seqs > fa::kMaxVarlenSeqs || total_q < 1) return 0;
+    // the tile list: a count, a pad, then (sequence, Q block) pairs; the bound
+    // on tiles holds for every Q block size the library uses (>= 128 rows)
+    const long long ints = 2 + 2 * fa::varlen_max_tiles(num_seqs, total_q, 128);
+    return ((size_t)ints * 4 + 255) / 256 * 256;
+}
+
+int fa_fwd_varlen(const void *q, const void *k, const void *v, void *out, float *lse, const int *cu_seqlens_q,
+                  const int *cu_seqlens_k, int num_seqs, int total_q, int total_k, int H, int d, float scale,
+                  int causal, int dtype, void *workspace, size_t ws_bytes, hipStream_t stream) {
+    if (!q || !k || !v || !out || !cu_seqlens_q || !cu_seqlens_k)
+        return fail(FA_ERR_INVALID_ARG, "q, k, v, out, cu_seqlens_q and cu_seqlens_k must be non-null");
+    if (num_seqs < 1 || total_q < 1 || total_k < 1 || H < 1 || d < 1)
+        return fail(FA_ERR_INVALID_ARG, "num_seqs, total_q, total_k, H and d must be >= 1");
+    if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+    if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (dtype != FA_F16 && dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "the variable-length path takes fp16 or bf16");
+    if (d != 32 && d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "d must be 32, 64 or 128");
+    if (num_seqs > fa::kMaxVarlenSeqs) return fail(FA_ERR_UNSUPPORTED, "num_seqs must be <= 8192");
+    if ((int64_t)total_q * H * d > INT32_MAX || (int64_t)total_k * H * d > INT32_MAX)
+        return fail(FA_ERR_UNSUPPORTED, "total_q*H*d and total_k*H*d must each fit in 31 bits");
+    if ((int64_t)H * fa::varlen_max_tiles(num_seqs, total_q, 128) > INT32_MAX)
+        return fail(FA_ERR_UNSUPPORTED, "too many tiles for one launch");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+        return fail(FA_ERR_UNSUPPORTED, "q, k, v and out must be 16-byte aligned");
+    if (!aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4) || (lse && !aligned(lse, 4)))
+        return fail(FA_ERR_UNSUPPORTED, "cu_seqlens_q, cu_seqlens_k and lse must be 4-byte aligned");
+    const size_t es = element_size(dtype);
+    const size_t q_bytes = (size_t)total_q * H * d * es, kv_bytes = (size_t)total_k * H * d * es;
+    const size_t lse_bytes = (size_t)H * total_q * 4, cu_bytes = (size_t)(num_seqs + 1) * 4;
+    const void *ins[5] = {q, k, v, cu_seqlens_q, cu_seqlens_k};
+    const size_t in_bytes[5] = {q_bytes, kv_bytes, kv_bytes, cu_bytes, cu_bytes};
+    for (int i = 0; i < 5; ++i) {
+        if (overlaps(out, q_bytes, ins[i], in_bytes[i])) return fail(FA_ERR_INVALID_ARG, "out overlaps an input");
+        if (lse && overlaps(lse, lse_bytes, ins[i], in_bytes[i]))
+            return fail(FA_ERR_INVALID_ARG, "lse overlaps an input");
+    }
+    if (lse && overlaps(lse, lse_bytes, out, q_bytes)) return fail(FA_ERR_INVALID_ARG, "lse overlaps out");
+    const size_t need = fa_varlen_workspace_bytes(num_seqs, total_q);
+    if (!workspace || !aligned(workspace, 16) || ws_bytes < need)
+        return fail(FA_ERR_WORKSPACE, "workspace must be 16-byte aligned and hold fa_varlen_workspace_bytes() = " +
+                                          std::to_string(need) + " bytes");
+    for (int i = 0; i < 5; ++i)
+        if (overlaps(workspace, need, ins[i], in_bytes[i])) return fail(FA_ERR_WORKSPACE, "workspace overlaps an input");
+    if (overlaps(workspace, need, out, q_bytes) || (lse && overlaps(workspace, need, lse, lse_bytes)))
+        return fail(FA_ERR_WORKSPACE, "workspace overlaps an output");
+    const float sl = (float)((double)scale * kLog2e);
+    return hip_status(fa::launch_prefill_varlen(dtype, d, causal != 0, prefill_shape(d), q, k, v, out, lse,
+                                                cu_seqlens_q, cu_seqlens_k, num_seqs, H, total_q, total_k, sl,
+                                                workspace, stream),
+                      "variable-length launch");
+}
+
 int fa_default_num_splits(int Nk) {
     if (Nk < 1) return 0;
     int s = (Nk + 255) / 256;

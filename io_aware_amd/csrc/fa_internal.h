@@ -29,6 +29,17 @@ hipError_t launch_prefill(int dtype, int d, bool causal, int shape,
                           void *out, float *lse, int BH, int Nq, int Nk,
                           float scale_log2, hipStream_t stream);
 
+// Packed variable-length batch through the same kernel: q [total_q, H, d],
+// k and v [total_k, H, d], out like q, lse [H, total_q]; cu_q, cu_k the
+// int32 offsets [S + 1] (device).  A schedule kernel first writes the tile
+// list into workspace (varlen_workspace_ints ints).
+constexpr int kMaxVarlenSeqs = 8192;
+long long varlen_max_tiles(int S, int total_q, int block_rows);
+hipError_t launch_prefill_varlen(int dtype, int d, bool causal, int shape, const void *q, const void *k,
+                                 const void *v, void *out, float *lse, const int *cu_q, const int *cu_k, int S,
+                                 int H, int total_q, int total_k, float scale_log2, void *workspace,
+                                 hipStream_t stream);
+
 // float32 tiled forward (vector ALU), Br = Bc = 64.
 hipError_t launch_prefill_f32(int d, bool causal, const void *q, const void *k,
                               const void *v, void *out, float *lse, int BH,

@@ -202,5 +202,19 @@ FA_HD void map_workgroup(int wg, int BH, int Tr, bool causal, int &bh, int &qblo
     qblock = causal ? (Tr - 1 - r) : r;
 }
 
+// ---------------------------------------------------------------------------
+// Packed variable-length batches: sequence s covers rows [cu[s], cu[s+1]) of
+// a tensor with ``total`` rows.  The offsets are clamped into [0, total] and
+// made non-decreasing, so inconsistent offsets give empty or shortened
+// sequences, never an access outside the tensor.
+// ---------------------------------------------------------------------------
+FA_HD void varlen_bounds(const int *cu, int s, int total, int &begin, int &end) {
+    int b = cu[s], e = cu[s + 1];
+    b = b < 0 ? 0 : (b > total ? total : b);
+    e = e < b ? b : (e > total ? total : e);
+    begin = b;
+    end = e;
+}
+
 }  // namespace layout
 }  // namespace fa

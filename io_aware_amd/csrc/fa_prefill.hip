@@ -65,6 +65,14 @@ struct PrefillArgs {
     int Nk;
     int Tr;            // Q row blocks per (batch, head)
     float scale_log2;  // scale * log2(e)
+    // packed variable-length batches (q [total_q, H, d], k and v
+    // [total_k, H, d], lse [H, total_q]; the tile list from the schedule)
+    const int *cu_q;
+    const int *cu_k;
+    const int *sched;  // [0] = tiles, then (sequence, Q block) pairs from index 2
+    int H;
+    int total_q;
+    int total_k;
 };
 
 // Bound on a lane's per-tile sum of P between rescales; it keeps every
@@ -72,7 +80,7 @@ struct PrefillArgs {
 constexpr float kHeldSumBound = 256.0f;
 constexpr float kLn2 = 0.693147180559945309417f;
 
-template <typename T, int D, bool CAUSAL, int NW, int QW, int BC, int OCC>
+template <typename T, int D, bool CAUSAL, int NW, int QW, int BC, int OCC, bool VARLEN>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC)))
 void prefill_kernel(PrefillArgs a) {
     using M = Mfma<T>;
@@ -103,17 +111,47 @@ void prefill_kernel(PrefillArgs a) {
     const int l32 = lane & 31;
     const int g = lane >> 5;
 
-    int bh, qblk;
-    layout::map_workgroup(blockIdx.x, a.BH, a.Tr, CAUSAL, bh, qblk);
-    const int Nq = a.Nq;
-    const int Nk = a.Nk;
+    // Work item: (batch*head, Q block) of a dense launch, or (head, tile of
+    // the schedule) of a packed variable-length launch.  RS is the element
+    // stride between consecutive rows of one head.
+    int qblk, Nq, Nk, RS;
+    const T *qp, *kp, *vp;
+    T *op;
+    float *lsep;
+    if constexpr (VARLEN) {
+        const int t = blockIdx.x / a.H;
+        const int h = blockIdx.x - t * a.H;
+        if (t >= a.sched[0]) return;  // the grid is an upper bound on the tiles (workgroup-uniform exit)
+        const int seq = a.sched[2 + 2 * t];
+        qblk = a.sched[3 + 2 * t];
+        int qs, qe, ks0, ke;
+        layout::varlen_bounds(a.cu_q, seq, a.total_q, qs, qe);
+        layout::varlen_bounds(a.cu_k, seq, a.total_k, ks0, ke);
+        Nq = qe - qs;
+        Nk = ke - ks0;
+        RS = a.H * D;
+        qp = static_cast<const T *>(a.q) + ((size_t)qs * a.H + h) * D;
+        kp = static_cast<const T *>(a.k) + ((size_t)ks0 * a.H + h) * D;
+        vp = static_cast<const T *>(a.v) + ((size_t)ks0 * a.H + h) * D;
+        op = static_cast<T *>(a.out) + ((size_t)qs * a.H + h) * D;
+        lsep = a.lse ? a.lse + (size_t)h * a.total_q + qs : nullptr;
+    } else {
+        int bh;
+        layout::map_workgroup(blockIdx.x, a.BH, a.Tr, CAUSAL, bh, qblk);
+        Nq = a.Nq;
+        Nk = a.Nk;
+        RS = D;
+        qp = static_cast<const T *>(a.q) + (size_t)bh * Nq * D;
+        kp = static_cast<const T *>(a.k) + (size_t)bh * Nk * D;
+        vp = static_cast<const T *>(a.v) + (size_t)bh * Nk * D;
+        op = static_cast<T *>(a.out) + (size_t)bh * Nq * D;
+        lsep = a.lse ? a.lse + (size_t)bh * Nq : nullptr;
+    }
+    const int RSB = RS * 2;  // bytes between rows
     const int q0 = qblk * BR;
     const int q0w = q0 + wave * QW;
-    const T *qp = static_cast<const T *>(a.q) + (size_t)bh * Nq * D;
-    const T *kp = static_cast<const T *>(a.k) + (size_t)bh * Nk * D;
-    const T *vp = static_cast<const T *>(a.v) + (size_t)bh * Nk * D;
     const float c = a.scale_log2;
-    const uint32_t kv_bytes = (uint32_t)Nk * ROW;
+    const uint32_t kv_bytes = Nk > 0 ? (uint32_t)(Nk - 1) * RSB + ROW : 0u;
     const __amdgpu_buffer_rsrc_t rsrc_k = __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(kp), (short)0, (int)kv_bytes, kBufferDword3);
     const __amdgpu_buffer_rsrc_t rsrc_v = __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(vp), (short)0, (int)kv_bytes, kBufferDword3);
 
@@ -123,9 +161,9 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int n = 0; n < NDMA; ++n) {
         const int u = (n * NW + wave) * 64 + lane;
-        kdma[n] = (uint32_t)layout::k_dma_src_elem<D>(u) * 2;
-        vdma[n] = (uint32_t)layout::v_dma_src_elem<D>(u) * 2;
         dkey[n] = u / CH;
+        kdma[n] = (uint32_t)(layout::k_dma_src_elem<D>(u) + dkey[n] * (RS - D)) * 2;
+        vdma[n] = (uint32_t)(layout::v_dma_src_elem<D>(u) + dkey[n] * (RS - D)) * 2;
     }
     // per-lane operand read offsets (bytes within a tile, block / k-step 0)
     int koff[KS], voff[DB];
@@ -137,7 +175,7 @@ void prefill_kernel(PrefillArgs a) {
     auto issue_tile = [&](int k0, int stage) {
         char *kbase = smem + stage * STAGE_BYTES;
         char *vbase = kbase + TILE_BYTES;
-        const uint32_t soff = (uint32_t)k0 * ROW;
+        const uint32_t soff = (uint32_t)k0 * RSB;
         const bool tail = k0 + BC > Nk;  // workgroup-uniform
 #pragma unroll
         for (int n = 0; n < NDMA; ++n) {
@@ -145,8 +183,8 @@ void prefill_kernel(PrefillArgs a) {
             if (tail) {
                 const int over = k0 + dkey[n] - (Nk - 1);  // rows past the end: fetch the last key instead
                 if (over > 0) {
-                    ko -= (uint32_t)over * ROW;
-                    vo -= (uint32_t)over * ROW;
+                    ko -= (uint32_t)over * RSB;
+                    vo -= (uint32_t)over * RSB;
                 }
             }
             const int dst = (n * NW + wave) * 1024;
@@ -164,7 +202,7 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             u32x4 raw = {0u, 0u, 0u, 0u};
-            if (row < Nq) raw = *reinterpret_cast<const u32x4 *>(qp + (size_t)row * D + 16 * ks + 8 * g);
+            if (row < Nq) raw = *reinterpret_cast<const u32x4 *>(qp + (size_t)row * RS + 16 * ks + 8 * g);
             qf[qb][ks] = __builtin_bit_cast(x8, raw);
         }
     }
@@ -303,16 +341,17 @@ void prefill_kernel(PrefillArgs a) {
         __syncthreads();                                    // ... and every thread's; stage S is free
     };
 
-    issue_tile(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    if (nt > 0) {  // workgroup-uniform; a sequence without keys has no tile
+        issue_tile(0, 0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
     for (int jt = 0; jt < nt; jt += 2) {
         step(Int<0>{}, jt);
         if (jt + 1 < nt) step(Int<1>{}, jt + 1);
     }
 
     // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2 --------------------
-    T *op = static_cast<T *>(a.out) + (size_t)bh * Nq * D;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const float l = xor32_sum(l_part[qb]);
@@ -327,58 +366,163 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) t[e] = oacc[qb][db][4 * rg + e] * inv;
                     const x4 o = __builtin_convertvector(t, x4);
-                    *reinterpret_cast<x4 *>(op + (size_t)row * D + 32 * db + 8 * rg + 4 * g) = o;
+                    *reinterpret_cast<x4 *>(op + (size_t)row * RS + 32 * db + 8 * rg + 4 * g) = o;
                 }
-            if (g == 0 && a.lse != nullptr)
-                a.lse[(size_t)bh * Nq + row] =
+            if (g == 0 && lsep != nullptr)
+                lsep[row] =
                     (l > 0.0f) ? (m_held[qb] + __builtin_amdgcn_logf(l)) * kLn2 : -__builtin_inff();
         }
     }
 }
 
+// ---------------------------------------------------------------------------
+// Tile schedule of a packed variable-length batch ("9.4 FlashAttention 与
+// FlashMLA" section 9.4.6: the work of every workgroup is fixed before the
+// attention launch, cutting sequences of different lengths into equal
+// tiles).  One workgroup lists the (sequence, Q block) tiles of Br queries
+// and orders them by their number of K/V blocks, longest first, so the
+// attention grid starts the long tiles first and the short ones fill the
+// tail.  Output: sched[0] = number of tiles, then the pairs from index 2.
+// ---------------------------------------------------------------------------
+constexpr int kSchedThreads = 1024;
+constexpr int kSchedBuckets = 1024;
+
+template <int BR, int BC, bool CAUSAL>
+__global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(const int *cu_q, const int *cu_k, int S,
+                                                                         int total_q, int total_k, int max_tiles,
+                                                                         int *sched) {
+    __shared__ int tile_start[kMaxVarlenSeqs + 1];
+    __shared__ int hist[kSchedBuckets];
+    __shared__ int scan[kSchedThreads];
+    __shared__ int wmax_s;
+    static_assert(kSchedBuckets == kSchedThreads, "one bucket per thread");
+    const int tid = threadIdx.x;
+    if (tid == 0) wmax_s = 0;
+    hist[tid] = 0;
+    __syncthreads();
+
+    // Q tiles per sequence, their exclusive prefix sum, and the longest K/V
+    // block count (for the bucket scale)
+    int carry = 0;
+    for (int base = 0; base < S; base += kSchedThreads) {
+        const int s = base + tid;
+        int nb = 0;
+        if (s < S) {
+            int qs, qe, ks, ke;
+            layout::varlen_bounds(cu_q, s, total_q, qs, qe);
+            layout::varlen_bounds(cu_k, s, total_k, ks, ke);
+            nb = (qe - qs + BR - 1) / BR;
+            atomicMax(&wmax_s, (ke - ks + BC - 1) / BC);
+        }
+        scan[tid] = nb;
+        __syncthreads();
+        for (int off = 1; off < kSchedThreads; off <<= 1) {
+            const int v = tid >= off ? scan[tid - off] : 0;
+            __syncthreads();
+            scan[tid] += v;
+            __syncthreads();
+        }
+        if (s < S) tile_start[s] = carry + scan[tid] - nb;
+        carry += scan[kSchedThreads - 1];
+        __syncthreads();
+    }
+    const int T = carry;
+    if (tid == 0) tile_start[S] = T;
+    __syncthreads();
+    const int wmax = wmax_s;
+
+    // tile t -> (sequence, Q block) and its descending-work bucket
+    auto locate = [&](int t, int &s, int &qb) {
+        int lo = 0, hi = S - 1;  // the last sequence whose first tile is <= t (it has tiles)
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (tile_start[mid] <= t) lo = mid;
+            else hi = mid - 1;
+        }
+        s = lo;
+        qb = t - tile_start[lo];
+        int qs, qe, ks, ke;
+        layout::varlen_bounds(cu_q, s, total_q, qs, qe);
+        layout::varlen_bounds(cu_k, s, total_k, ks, ke);
+        const int nk = ke - ks;
+        const int kv_end = CAUSAL ? min(nk, (qb + 1) * BR) : nk;
+        const int work = (kv_end + BC - 1) / BC;
+        const int b = wmax > 0 ? (int)((long long)work * (kSchedBuckets - 1) / wmax) : 0;
+        return kSchedBuckets - 1 - b;
+    };
+    for (int t = tid; t < T; t += kSchedThreads) {
+        int s, qb;
+        atomicAdd(&hist[locate(t, s, qb)], 1);
+    }
+    __syncthreads();
+    // exclusive prefix sum of the bucket sizes
+    const int own = hist[tid];
+    scan[tid] = own;
+    __syncthreads();
+    for (int off = 1; off < kSchedThreads; off <<= 1) {
+        const int v = tid >= off ? scan[tid - off] : 0;
+        __syncthreads();
+        scan[tid] += v;
+        __syncthreads();
+    }
+    hist[tid] = scan[tid] - own;
+    __syncthreads();
+    for (int t = tid; t < T; t += kSchedThreads) {
+        int s, qb;
+        const int pos = atomicAdd(&hist[locate(t, s, qb)], 1);
+        if (pos < max_tiles) {  // only offsets that decrease (overlapping sequences) can exceed the bound
+            sched[2 + 2 * pos] = s;
+            sched[3 + 2 * pos] = qb;
+        }
+    }
+    if (tid == 0) sched[0] = T < max_tiles ? T : max_tiles;
+}
+
 template <typename T, int D, bool CAUSAL, int NW, int QW, int OCC, int BC = 64>
-hipError_t launch_one(const void *q, const void *k, const void *v, void *out, float *lse, int BH, int Nq, int Nk,
-                      float scale_log2, hipStream_t stream) {
+hipError_t launch_one(const PrefillArgs &base, bool varlen, int S, hipStream_t stream) {
     constexpr int BR = NW * QW;
-    PrefillArgs a;
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.out = out;
-    a.lse = lse;
-    a.BH = BH;
-    a.Nq = Nq;
-    a.Nk = Nk;
-    a.Tr = (Nq + BR - 1) / BR;
-    a.scale_log2 = scale_log2;
-    const long long nwg = (long long)BH * a.Tr;
-    if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((prefill_kernel<T, D, CAUSAL, NW, QW, BC, OCC>), dim3((unsigned)nwg), dim3(NW * 64), 0,
+    PrefillArgs a = base;
+    if (!varlen) {
+        a.Tr = (a.Nq + BR - 1) / BR;
+        const long long nwg = (long long)a.BH * a.Tr;
+        if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((prefill_kernel<T, D, CAUSAL, NW, QW, BC, OCC, false>), dim3((unsigned)nwg),
+                           dim3(NW * 64), 0, stream, a);
+        return hipGetLastError();
+    }
+    const long long tiles = varlen_max_tiles(S, a.total_q, BR);
+    const long long nwg = (long long)a.H * tiles;
+    if (nwg > 0x7fffffffLL || S < 1 || S > kMaxVarlenSeqs) return hipErrorInvalidConfiguration;
+    int *sched = const_cast<int *>(a.sched);
+    hipLaunchKernelGGL((varlen_schedule_kernel<BR, BC, CAUSAL>), dim3(1), dim3(kSchedThreads), 0, stream, a.cu_q,
+                       a.cu_k, S, a.total_q, a.total_k, (int)tiles, sched);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((prefill_kernel<T, D, CAUSAL, NW, QW, BC, OCC, true>), dim3((unsigned)nwg), dim3(NW * 64), 0,
                        stream, a);
     return hipGetLastError();
 }
 
 template <typename T, int D, bool CAUSAL>
-hipError_t launch_shape(int shape, const void *q, const void *k, const void *v, void *out, float *lse, int BH,
-                        int Nq, int Nk, float sl, hipStream_t stream) {
+hipError_t launch_shape(int shape, const PrefillArgs &a, bool varlen, int S, hipStream_t stream) {
     switch (shape) {
-        case kShapeW4Q32: return launch_one<T, D, CAUSAL, 4, 32, 2>(q, k, v, out, lse, BH, Nq, Nk, sl, stream);
-        case kShapeW4Q64: return launch_one<T, D, CAUSAL, 4, 64, 1>(q, k, v, out, lse, BH, Nq, Nk, sl, stream);
-        case kShapeW2Q64: return launch_one<T, D, CAUSAL, 2, 64, 1>(q, k, v, out, lse, BH, Nq, Nk, sl, stream);
+        case kShapeW4Q32: return launch_one<T, D, CAUSAL, 4, 32, 2>(a, varlen, S, stream);
+        case kShapeW4Q64: return launch_one<T, D, CAUSAL, 4, 64, 1>(a, varlen, S, stream);
+        case kShapeW2Q64: return launch_one<T, D, CAUSAL, 2, 64, 1>(a, varlen, S, stream);
         case kShapeW4Q32B32:  // a 32-key tile of d = 32 is too small to split over 256 threads
-            if constexpr (D >= 64) return launch_one<T, D, CAUSAL, 4, 32, 3, 32>(q, k, v, out, lse, BH, Nq, Nk, sl, stream);
-            else return launch_one<T, D, CAUSAL, 4, 32, 2>(q, k, v, out, lse, BH, Nq, Nk, sl, stream);
+            if constexpr (D >= 64) return launch_one<T, D, CAUSAL, 4, 32, 3, 32>(a, varlen, S, stream);
+            else return launch_one<T, D, CAUSAL, 4, 32, 2>(a, varlen, S, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <typename T>
-hipError_t launch_typed(int d, bool causal, int shape, const void *q, const void *k, const void *v, void *out,
-                        float *lse, int BH, int Nq, int Nk, float sl, hipStream_t stream) {
-#define FA_CASE(DD)                                                                                  \
-    case DD:                                                                                         \
-        return causal ? launch_shape<T, DD, true>(shape, q, k, v, out, lse, BH, Nq, Nk, sl, stream)  \
-                      : launch_shape<T, DD, false>(shape, q, k, v, out, lse, BH, Nq, Nk, sl, stream);
+hipError_t launch_typed(int d, bool causal, int shape, const PrefillArgs &a, bool varlen, int S,
+                        hipStream_t stream) {
+#define FA_CASE(DD)                                                                 \
+    case DD:                                                                        \
+        return causal ? launch_shape<T, DD, true>(shape, a, varlen, S, stream)      \
+                      : launch_shape<T, DD, false>(shape, a, varlen, S, stream);
     switch (d) {
         FA_CASE(32)
         FA_CASE(64)
@@ -386,6 +530,13 @@ hipError_t launch_typed(int d, bool causal, int shape, const void *q, const void
         default: return hipErrorInvalidValue;
     }
 #undef FA_CASE
+}
+
+hipError_t launch_any(int dtype, int d, bool causal, int shape, const PrefillArgs &a, bool varlen, int S,
+                      hipStream_t stream) {
+    if (dtype == 2) return launch_typed<__bf16>(d, causal, shape, a, varlen, S, stream);
+    if (dtype == 1) return launch_typed<_Float16>(d, causal, shape, a, varlen, S, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -400,13 +551,44 @@ int prefill_block_rows(int shape) {
     }
 }
 
+long long varlen_max_tiles(int S, int total_q, int block_rows) {
+    // sum_s ceil(len_s / Br) <= total_q / Br + S
+    return ((long long)total_q + block_rows - 1) / block_rows + S;
+}
+
 hipError_t launch_prefill(int dtype, int d, bool causal, int shape, const void *q, const void *k, const void *v,
                           void *out, float *lse, int BH, int Nq, int Nk, float scale_log2, hipStream_t stream) {
-    if (dtype == 2)
-        return launch_typed<__bf16>(d, causal, shape, q, k, v, out, lse, BH, Nq, Nk, scale_log2, stream);
-    if (dtype == 1)
-        return launch_typed<_Float16>(d, causal, shape, q, k, v, out, lse, BH, Nq, Nk, scale_log2, stream);
-    return hipErrorInvalidValue;
+    PrefillArgs a = {};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.lse = lse;
+    a.BH = BH;
+    a.Nq = Nq;
+    a.Nk = Nk;
+    a.scale_log2 = scale_log2;
+    return launch_any(dtype, d, causal, shape, a, false, 0, stream);
+}
+
+hipError_t launch_prefill_varlen(int dtype, int d, bool causal, int shape, const void *q, const void *k,
+                                 const void *v, void *out, float *lse, const int *cu_q, const int *cu_k, int S,
+                                 int H, int total_q, int total_k, float scale_log2, void *workspace,
+                                 hipStream_t stream) {
+    PrefillArgs a = {};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.lse = lse;
+    a.scale_log2 = scale_log2;
+    a.cu_q = cu_q;
+    a.cu_k = cu_k;
+    a.sched = static_cast<const int *>(workspace);
+    a.H = H;
+    a.total_q = total_q;
+    a.total_k = total_k;
+    return launch_any(dtype, d, causal, shape, a, true, S, stream);
 }
 
 }  // namespace fa

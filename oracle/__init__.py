@@ -250,7 +250,8 @@ def attention_bwd(q, k, v, dout, scale: float, causal: bool, heads=None, q_idx=N
     return (dq, dk, dv, delta) if with_delta else (dq, dk, dv)
 
 
-def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: bool, seqs=None, threads: int = 0):
+def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: bool, seqs=None, rows=None,
+                     threads: int = 0):
     """Exact attention over packed variable-length sequences, in fp64.
 
     q: [total_q, H, d]; k, v: [total_k, H, d] (token-major, heads inside);
@@ -258,7 +259,8 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: 
     Sequence s is q[cu_q[s]:cu_q[s+1]] attending to k, v[cu_k[s]:cu_k[s+1]]
     with ``attention`` (causal: top-left within the sequence).  A query with
     no key gets O = 0 and LSE = -inf.  ``seqs`` restricts the work to some
-    sequences (the other rows of the result stay NaN).
+    sequences (the other rows of the result stay NaN); ``rows`` maps a
+    sequence to the query indices within it to compute (all if absent).
 
     Returns (out [total_q, H, d], lse [H, total_q]), float64.
     """
@@ -281,6 +283,16 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: 
         qs = np.ascontiguousarray(qa[a:b].transpose(1, 0, 2))[None]      # [1, H, n, d]
         ks = np.ascontiguousarray(ka[ka_:kb_].transpose(1, 0, 2))[None]
         vs = np.ascontiguousarray(va[ka_:kb_].transpose(1, 0, 2))[None]
+        if rows is not None and s in rows:
+            n = b - a
+            ri = np.asarray(rows[s], dtype=np.int64)
+            flat = (np.arange(H, dtype=np.int64)[:, None] * n + ri[None, :]).reshape(-1)   # head-major
+            o, l = attention(qs, ks, vs, scale, causal, rows=flat, threads=threads)
+            o = o.reshape(H, ri.size, d)
+            l = l.reshape(H, ri.size)
+            out[a + ri] = o.transpose(1, 0, 2)
+            lse[:, a + ri] = l
+            continue
         o, l = attention(qs, ks, vs, scale, causal, threads=threads)
         out[a:b] = o[0].transpose(1, 0, 2)
         lse[:, a:b] = l[0]

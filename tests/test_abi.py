@@ -39,7 +39,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for want in ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_paged_decode", "fa_splitkv_workspace_bytes", "fa_status_string",
+    for want in ("fa_fwd", "fa_fwd_varlen", "fa_varlen_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_paged_decode", "fa_splitkv_workspace_bytes", "fa_status_string",
                  "fa_last_error", "fa_release_workspace", "fa_default_num_splits", "fa_map_workgroup"):
         assert want in names
 
@@ -242,3 +242,39 @@ def test_bwd_workspace_bytes(fa):
     assert fa.fa_bwd_workspace_bytes(1, 1, 1, 48) == 0
     assert fa.fa_bwd_workspace_bytes(0, 1, 1, 64) == 0
     assert call_bwd(fa, ws_bytes=fa.fa_bwd_workspace_bytes(2, 4, 100, 64) - 1) == 4
+
+
+VQ, VK, VV, VO, VL, VCQ, VCK, VW = (0x10000000 * i for i in range(22, 30))
+VGOOD = dict(q=VQ, k=VK, v=VV, out=VO, lse=VL, cq=VCQ, ck=VCK, S=4, total_q=1000, total_k=900, H=8, d=128,
+             scale=0.125, causal=1, dtype=2, ws=VW)
+
+
+def call_varlen(fa, ws_bytes=None, **over):
+    a = dict(VGOOD)
+    a.update(over)
+    if ws_bytes is None:
+        ws_bytes = fa.fa_varlen_workspace_bytes(max(1, min(a["S"], 8192)), max(1, a["total_q"]))
+    return fa.lib.fa_fwd_varlen(a["q"], a["k"], a["v"], a["out"], a["lse"], a["cq"], a["ck"], a["S"],
+                                a["total_q"], a["total_k"], a["H"], a["d"], a["scale"], a["causal"], a["dtype"],
+                                a["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), 1), (dict(cq=None), 1), (dict(ck=None), 1), (dict(out=None), 1), (dict(S=0), 1),
+    (dict(total_q=0), 1), (dict(total_k=0), 1), (dict(H=0), 1), (dict(scale=-1.0), 1), (dict(causal=2), 1),
+    (dict(dtype=0), 2), (dict(d=80), 2), (dict(S=8193), 2), (dict(total_q=1 << 25), 2),
+    (dict(q=VQ + 8), 2), (dict(cq=VCQ + 2), 2), (dict(lse=VL + 1), 2),
+    (dict(out=VK + 64), 1), (dict(lse=VCQ), 1), (dict(lse=VO + 16), 1),
+    (dict(ws=None), 4), (dict(ws=VW + 4), 4), (dict(ws=VO), 4), (dict(ws=VCK), 4),
+])
+def test_varlen_rejects_invalid_arguments(fa, over, code):
+    assert call_varlen(fa, **over) == code
+    assert fa.fa_last_error() != ""
+
+
+def test_varlen_workspace_bytes(fa):
+    # 4 * (2 + 2 * (ceil(1000 / 128) + 4)) = 104 -> 256
+    assert fa.fa_varlen_workspace_bytes(4, 1000) == 256
+    assert fa.fa_varlen_workspace_bytes(16, 70000) == ((2 + 2 * (547 + 16)) * 4 + 255) // 256 * 256
+    assert fa.fa_varlen_workspace_bytes(0, 10) == 0 and fa.fa_varlen_workspace_bytes(9000, 10) == 0
+    assert call_varlen(fa, ws_bytes=100) == 4

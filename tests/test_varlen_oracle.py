@@ -89,3 +89,14 @@ def test_empty_sequences():
     o2, l2 = oracle.varlen_attention(q[:5], k[:4], v[:4], cq2, ck2, 0.3, False)
     assert (o2[:3] == 0).all() and np.isneginf(l2[:, :3]).all()
     assert np.isfinite(l2[:, 3:]).all()
+
+
+def test_selected_rows_match_full():
+    w = fa_inputs.VarlenWorkload("t", 3, 2, 16, "f32", True, 5, 20, 60)
+    q, k, v, cq, ck = fa_inputs.make_varlen(w)
+    full = oracle.varlen_attention(q, k, v, cq, ck, 0.3, True)
+    part = oracle.varlen_attention(q, k, v, cq, ck, 0.3, True, rows={1: [0, 5, int(cq[2] - cq[1]) - 1]})
+    a = int(cq[1])
+    for i in (0, 5, int(cq[2] - cq[1]) - 1):
+        np.testing.assert_array_equal(part[0][a + i], full[0][a + i])
+        np.testing.assert_array_equal(part[1][:, a + i], full[1][:, a + i])
