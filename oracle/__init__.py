@@ -28,6 +28,10 @@ Two parts:
   different lengths: each sequence, cut out of the packed tensors by its
   cumulative offsets, goes through ``attention`` on its own.  Source: "9.4
   FlashAttention 与 FlashMLA" section 9.4.6 (variable-length batches).
+* ``oracle.fp8`` -- the FP8 mode: incoherent processing (a random
+  orthogonal transform of Q and K), per-head E4M3 quantisation in float32,
+  then exact attention on the dequantised values.  Source: "9.4
+  FlashAttention 与 FlashMLA" section 9.4.4.
 * ``oracle.algorithms`` -- the pages' algorithms (one-pass online softmax,
   blocked forward with deferred or per-step normalisation, split-KV partials
   and their merge) in numpy fp64.  They exist to pin ``attention`` and each
