@@ -33,11 +33,13 @@ sys.path.insert(0, ROOT)
 
 DEFAULT_WORKLOAD = "prefill_causal_bf16_b8h16_n4096_d128"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector (packed)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 KERNEL_SOURCES = ["io_aware_amd/csrc/fa_prefill.hip", "io_aware_amd/csrc/fa_layout.h",
                   "io_aware_amd/csrc/fa_decode.hip", "io_aware_amd/csrc/fa_f32.hip",
-                  "io_aware_amd/csrc/fa_backward.hip", "io_aware_amd/csrc/fa_device.h"]
+                  "io_aware_amd/csrc/fa_backward.hip", "io_aware_amd/csrc/fa_device.h",
+                  "io_aware_amd/csrc/fa_fp8.hip"]
 
 
 def workload_flops(w) -> float:
@@ -48,6 +50,8 @@ def workload_flops(w) -> float:
 
 
 def workload_bytes(w) -> float:
+    if w.fp8:  # read the E4M3 q, k, v codes; write O (16-bit) and LSE
+        return float(w.B * w.H * (w.Nq * w.d + 2 * w.Nk * w.d + 2 * w.Nq * w.d) + 4 * w.B * w.H * w.Nq)
     es = 4 if w.dtype == "f32" else 2
     if w.backward:  # read q, k, v, out, dout, lse; write dq, dk, dv
         return float(es * w.B * w.H * (5 * w.Nq * w.d + 4 * w.Nk * w.d) + 4 * w.B * w.H * w.Nq)
@@ -166,7 +170,16 @@ def run_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s=0.3):
     qd, kd, vd = (t.to(dev).contiguous() for t in (q, k, v))
     out = torch.empty_like(qd)
     lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
-    if w.backward:
+    extra = {}
+    if w.fp8:
+        signs = fa_inputs.make_signs(w.d, w.seed).to(dev)
+        pack = fa.fa_quantize_fp8(qd, kd, vd, signs=signs)
+        qms, _ = time_steps(lambda: fa.fa_quantize_fp8(qd, kd, vd, signs=signs, pack=pack), 5, 1, 0.0)
+        extra["quantize_ms"] = qms
+
+        def step():
+            fa.fa_fwd_fp8(pack, w.B, w.H, w.Nq, w.Nk, w.d, scale=w.scale, causal=w.causal, out=out, lse=lse)
+    elif w.backward:
         fa.fa_fwd(qd, kd, vd, scale=w.scale, causal=w.causal, out=out, lse=lse)
         dod = fa_inputs.make_dout(w.B, w.H, w.Nq, w.d, w.dtype, w.seed).to(dev)
         dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
@@ -193,7 +206,7 @@ def run_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s=0.3):
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS}
     else:
-        peak = PEAK_FP32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+        peak = PEAK_FP32_TFLOPS if w.dtype == "f32" else (PEAK_FP8_TFLOPS if w.fp8 else PEAK_BF16_TFLOPS)
         achieved = flops / (kernel_ms * 1e-3) / 1e12
         roof = {"bound": "mfma" if w.dtype != "f32" else "alu", "achieved": achieved, "peak": peak,
                 "unit": "TFLOP/s", "frac": achieved / peak}
@@ -203,12 +216,14 @@ def run_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s=0.3):
         "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, "prewarm_s": prewarm_s,
         "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded randn, cast with RNE)",
+        "vs_baseline": None, "dtype": "e4m3" if w.fp8 else w.dtype,
+        "data": "synthetic (seeded randn, cast with RNE)",
         "config": {"workload": name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
                    "causal": w.causal, "dtype": w.dtype, "q_sigma": w.q_sigma, "num_splits": w.num_splits,
                    "flop_per_step": flops, "algorithmic_bytes_per_step": nbytes},
         "roofline": roof,
     }
+    rec.update(extra)
     if with_cpu:
         rec["cpu_baseline"] = cpu_baseline(w, q, k, v, cpu_target_s)
     return rec

@@ -40,6 +40,7 @@ class Workload:
     q_sigma: float = 1.0
     num_splits: int = 0          # > 0: run through the explicit split-KV entry point
     backward: bool = False       # the workload of the backward pass (forward output and LSE, then gradients)
+    fp8: bool = False            # the FP8 forward on the quantised pack (incoherent processing on)
     note: str = field(default="", compare=False)
 
     @property
@@ -70,6 +71,8 @@ WORKLOADS = {
                  num_splits=32),
         Workload("bwd_causal_bf16_b8h16_n4096_d128", 8, 16, 4096, 4096, 128, "bf16", True, 1008, backward=True,
                  note="the causal prefill shapes, backward"),
+        Workload("fp8_causal_b8h16_n4096_d128", 8, 16, 4096, 4096, 128, "bf16", True, 1011, fp8=True,
+                 note="the causal prefill shapes, E4M3 inputs"),
     ]
 }
 
@@ -254,6 +257,13 @@ def make_qkv(B: int, H: int, Nq: int, Nk: int, d: int, dtype, seed: int,
 
 def make_workload(w: Workload):
     return make_qkv(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.seed, w.q_sigma)
+
+
+def make_signs(d: int, seed: int):
+    """The random signs of the incoherent transform: float32 [d] of +-1 from a
+    CPU generator seeded with seed + 600000 (a fair coin per element)."""
+    g = torch.Generator().manual_seed(int(seed) + 600000)
+    return torch.where(torch.rand(d, generator=g) < 0.5, -1.0, 1.0).to(torch.float32)
 
 
 def make_dout(B: int, H: int, Nq: int, d: int, dtype, seed: int):

@@ -179,6 +179,54 @@ int fa_fwd_varlen(const void *q, const void *k, const void *v, void *out,
                   size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * FP8 forward ("9.4 FlashAttention 与 FlashMLA" section 9.4.4: attention
+ * with 8-bit E4M3 inputs; Q and K first multiplied by one random orthogonal
+ * matrix so that the quantisation error is spread evenly, "incoherent
+ * processing").  Two calls: fa_quantize_fp8 turns fp16/bf16 q, k, v into a
+ * "pack" of E4M3 codes, fa_fwd_fp8 runs attention on a pack.  d = 64 or 128.
+ *
+ * Pack layout (BH = B*H, Nkp = Nk rounded up to a multiple of 64, up(x) = x
+ * rounded up to 256; byte offsets from the pack's start):
+ *   q8      at 0:                          [BH, Nq, d]  Q M codes
+ *   k8      at up(BH*Nq*d):                [BH, Nkp, d] K M codes (rows >= Nk zero)
+ *   v8t     at k8 + up(BH*Nkp*d):          [BH, d, Nkp] V codes transposed; within
+ *           each group of 64 keys, position p = 32*g + 16*b + r holds key
+ *           32*b + 8*(r/4) + 4*g + (r%4) (g, b in {0,1}, r in 0..15), the order
+ *           in which the forward kernel holds probabilities; keys >= Nk zero
+ *   descale at v8t + up(BH*d*Nkp):         float [3][BH]: amax/448 of Q M, K M, V
+ *   scratch at descale + up(3*BH*4):       3*BH words used during quantisation
+ *   total   fa_fp8_pack_bytes(B, H, Nq, Nk, d) = scratch + up(3*BH*4).
+ * Codes are RNE_E4M3(clamp(x * 448/amax, -448, 448)), amax = max |x| over the
+ * (batch, head) (descale 1 for an all-zero head).
+ */
+size_t fa_fp8_pack_bytes(int B, int H, int Nq, int Nk, int d);
+
+/*
+ * fa_quantize_fp8 -- q [B, H, Nq, d], k and v [B, H, Nk, d] (dtype fp16 or
+ * bf16) -> pack.  signs: device float [d] of +-1 (the random diagonal of
+ * M = H_d diag(signs) / sqrt(d), H_d the Sylvester-Hadamard matrix), or NULL
+ * for no transform (M = I).  The transform is the fast Walsh-Hadamard
+ * butterfly in float32.  pack: at least fa_fp8_pack_bytes bytes, 256-byte
+ * aligned, not overlapping the inputs.
+ */
+int fa_quantize_fp8(const void *q, const void *k, const void *v,
+                    const float *signs, int B, int H, int Nq, int Nk, int d,
+                    int dtype, void *pack, size_t pack_bytes,
+                    hipStream_t stream);
+
+/*
+ * fa_fwd_fp8 -- attention on a pack: O = softmax(scale * Q' K'^T [+ mask]) V'
+ * with Q' = q8 * descale_q, K' = k8 * descale_k, V' = v8 * descale_v (so
+ * Q' K'^T approximates Q K^T; M cancels).  Both products run on the E4M3
+ * MFMA with float32 accumulation; P is rounded to E4M3 before P V'.  out:
+ * [B, H, Nq, d] in out_dtype (fp16 or bf16); lse: [B, H, Nq] float32 or NULL.
+ * The pack must come from fa_quantize_fp8 with the same B, H, Nq, Nk, d.
+ */
+int fa_fwd_fp8(const void *pack, void *out, float *lse, int B, int H, int Nq,
+               int Nk, int d, float scale, int causal, int out_dtype,
+               hipStream_t stream);
+
+/*
  * fa_bwd_workspace_bytes -- bytes of workspace fa_bwd needs: two float32
  * values per query row (the statistic LSE*log2(e) and D, see fa_bwd) plus a
  * padding of 64 rows, rounded up to 256 bytes.  Returns 0 for arguments

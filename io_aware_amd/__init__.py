@@ -42,6 +42,11 @@ _SIGNATURES = {
                                                                                   ctypes.c_int, ctypes.c_void_p,
                                                                                   ctypes.c_size_t,
                                                                                   ctypes.c_void_p]),
+    "fa_fp8_pack_bytes": (ctypes.c_size_t, [ctypes.c_int] * 5),
+    "fa_quantize_fp8": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int] * 6 + [ctypes.c_void_p, ctypes.c_size_t,
+                                                                                   ctypes.c_void_p]),
+    "fa_fwd_fp8": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int,
+                                                                              ctypes.c_int, ctypes.c_void_p]),
     "fa_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
     "fa_bwd": (ctypes.c_int, [ctypes.c_void_p] * 9 + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int,
                                                                            ctypes.c_int, ctypes.c_void_p,
@@ -238,6 +243,41 @@ def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale=None, causal=False,
     return out, lse
 
 
+def fa_fp8_pack_bytes(B, H, Nq, Nk, d) -> int:
+    return int(lib.fa_fp8_pack_bytes(B, H, Nq, Nk, d))
+
+
+def fa_quantize_fp8(q, k, v, signs=None, pack=None, stream=None):
+    """q [B, H, Nq, d], k and v [B, H, Nk, d] (fp16 / bf16) -> the E4M3 pack
+    (a uint8 device tensor of fa_fp8_pack_bytes bytes).  ``signs``: a float32
+    device tensor [d] of +-1 for the incoherent transform, or None."""
+    import torch
+    B, H, Nq, Nk, d = _shapes(q, k, v)
+    need = fa_fp8_pack_bytes(B, H, Nq, Nk, d)
+    if pack is None:
+        pack = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if signs is not None and (signs.dtype != torch.float32 or signs.numel() != d or not signs.is_cuda):
+        raise ValueError("signs must be a float32 device tensor of d elements")
+    _check(lib.fa_quantize_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(signs), B, H, Nq, Nk, d, _dtype_code(q), _ptr(pack),
+                               pack.numel() * pack.element_size(), _stream_handle(q, stream)), "fa_quantize_fp8")
+    return pack
+
+
+def fa_fwd_fp8(pack, B, H, Nq, Nk, d, scale=None, causal=False, out_dtype=None, out=None, lse=None,
+               return_lse=True, stream=None):
+    """Attention on an E4M3 pack.  Returns (out [B, H, Nq, d], lse [B, H, Nq])."""
+    import torch
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=out_dtype or torch.bfloat16, device=pack.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=pack.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check(lib.fa_fwd_fp8(_ptr(pack), _ptr(out), _ptr(lse), B, H, Nq, Nk, d, float(scale), 1 if causal else 0,
+                          _dtype_code(out), _stream_handle(out, stream)), "fa_fwd_fp8")
+    return out, lse
+
+
 def fa_bwd_workspace_bytes(B, H, Nq, d) -> int:
     return int(lib.fa_bwd_workspace_bytes(B, H, Nq, d))
 
@@ -297,6 +337,6 @@ def fa_version() -> int:
     return int(lib.fa_version())
 
 
-__all__ = ["fa_fwd", "fa_fwd_varlen", "fa_varlen_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_paged_decode", "fa_splitkv_workspace_bytes", "fa_default_num_splits",
+__all__ = ["fa_fwd", "fa_fwd_fp8", "fa_quantize_fp8", "fa_fp8_pack_bytes", "fa_fwd_varlen", "fa_varlen_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_paged_decode", "fa_splitkv_workspace_bytes", "fa_default_num_splits",
            "fa_release_workspace", "fa_map_workgroup", "fa_status_string", "fa_last_error", "fa_version",
            "FAError", "FA_F32", "FA_F16", "FA_BF16", "lib", "LIB_PATH"]

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_api.hip", "fa_prefill.hip", "fa_f32.hip", "fa_decode.hip", "fa_backward.hip"]
+SOURCES = ["fa_api.hip", "fa_prefill.hip", "fa_f32.hip", "fa_decode.hip", "fa_backward.hip", "fa_fp8.hip"]
 
 
 def hipcc() -> str:

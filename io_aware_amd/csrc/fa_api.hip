@@ -339,6 +339,65 @@ int fa_fwd_varlen(const void *q, const void *k, const void *v, void *out, float 
                       "variable-length launch");
 }
 
+size_t fa_fp8_pack_bytes(int B, int H, int Nq, int Nk, int d) {
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || (d != 64 && d != 128)) return 0;
+    if ((int64_t)B * H > INT32_MAX) return 0;
+    return fa::fp8_layout(B * H, Nq, Nk, d).bytes;
+}
+
+// Checks shared by the two FP8 entry points.
+static int check_fp8_sizes(int B, int H, int Nq, int Nk, int d) {
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1)
+        return fail(FA_ERR_INVALID_ARG, "B, H, Nq, Nk and d must all be >= 1");
+    if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "the FP8 path takes d = 64 or 128");
+    const int64_t nkp = ((int64_t)Nk + 63) / 64 * 64;
+    if ((int64_t)B * H > INT32_MAX || (int64_t)Nq * d > INT32_MAX || nkp * d > INT32_MAX)
+        return fail(FA_ERR_UNSUPPORTED, "B*H, Nq*d and Nk*d must each fit in 31 bits");
+    return FA_OK;
+}
+
+int fa_quantize_fp8(const void *q, const void *k, const void *v, const float *signs, int B, int H, int Nq, int Nk,
+                    int d, int dtype, void *pack, size_t pack_bytes, hipStream_t stream) {
+    if (!q || !k || !v || !pack) return fail(FA_ERR_INVALID_ARG, "q, k, v and pack must be non-null");
+    int st = check_fp8_sizes(B, H, Nq, Nk, d);
+    if (st != FA_OK) return st;
+    if (dtype != FA_F16 && dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "the FP8 quantisation takes fp16 or bf16");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(pack, 256))
+        return fail(FA_ERR_UNSUPPORTED, "q, k and v must be 16-byte aligned and pack 256-byte aligned");
+    if (signs && !aligned(signs, 4)) return fail(FA_ERR_UNSUPPORTED, "signs must be 4-byte aligned");
+    const size_t need = fa_fp8_pack_bytes(B, H, Nq, Nk, d);
+    if (pack_bytes < need)
+        return fail(FA_ERR_WORKSPACE, "pack must hold fa_fp8_pack_bytes() = " + std::to_string(need) + " bytes");
+    const size_t bh = (size_t)B * H;
+    const size_t q_bytes = bh * Nq * d * 2, kv_bytes = bh * Nk * d * 2;
+    if (overlaps(pack, need, q, q_bytes) || overlaps(pack, need, k, kv_bytes) || overlaps(pack, need, v, kv_bytes) ||
+        (signs && overlaps(pack, need, signs, (size_t)d * 4)))
+        return fail(FA_ERR_INVALID_ARG, "pack overlaps an input");
+    return hip_status(fa::launch_fp8_quantize(dtype, d, q, k, v, signs, pack, B * H, Nq, Nk, stream),
+                      "FP8 quantisation launch");
+}
+
+int fa_fwd_fp8(const void *pack, void *out, float *lse, int B, int H, int Nq, int Nk, int d, float scale,
+               int causal, int out_dtype, hipStream_t stream) {
+    if (!pack || !out) return fail(FA_ERR_INVALID_ARG, "pack and out must be non-null");
+    int st = check_fp8_sizes(B, H, Nq, Nk, d);
+    if (st != FA_OK) return st;
+    if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+    if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (out_dtype != FA_F16 && out_dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "out must be fp16 or bf16");
+    if (!aligned(pack, 256) || !aligned(out, 16) || (lse && !aligned(lse, 4)))
+        return fail(FA_ERR_UNSUPPORTED, "pack must be 256-byte aligned, out 16-byte and lse 4-byte aligned");
+    const size_t need = fa_fp8_pack_bytes(B, H, Nq, Nk, d);
+    const size_t bh = (size_t)B * H;
+    const size_t o_bytes = bh * Nq * d * 2, lse_bytes = bh * Nq * 4;
+    if (overlaps(out, o_bytes, pack, need) || (lse && overlaps(lse, lse_bytes, pack, need)) ||
+        (lse && overlaps(lse, lse_bytes, out, o_bytes)))
+        return fail(FA_ERR_INVALID_ARG, "out and lse must not overlap the pack or each other");
+    const float sl = (float)((double)scale * kLog2e);
+    return hip_status(fa::launch_fp8_fwd(out_dtype, d, causal != 0, pack, out, lse, B * H, Nq, Nk, sl, stream),
+                      "FP8 forward launch");
+}
+
 int fa_default_num_splits(int Nk) {
     if (Nk < 1) return 0;
     int s = (Nk + 255) / 256;

@@ -60,6 +60,18 @@ hipError_t launch_paged_decode(int dtype, int d, const void *q, const void *k_ca
                                int log2_block, int max_blocks, int num_blocks, float scale_log2, int num_splits,
                                void *workspace, hipStream_t stream);
 
+// FP8 pack (the output of the quantisation step, the input of the FP8
+// forward): byte offsets of its parts for BH heads.
+struct Fp8Layout {
+    size_t q8, k8, v8t, descale, amax, bytes;
+    int Nkp;  // keys rounded up to the 64-key group
+};
+Fp8Layout fp8_layout(int BH, int Nq, int Nk, int d);
+hipError_t launch_fp8_quantize(int dtype, int d, const void *q, const void *k, const void *v, const float *signs,
+                               void *pack, int BH, int Nq, int Nk, hipStream_t stream);
+hipError_t launch_fp8_fwd(int out_dtype, int d, bool causal, const void *pack, void *out, float *lse, int BH,
+                          int Nq, int Nk, float scale_log2, hipStream_t stream);
+
 // Backward (bf16 / fp16, MFMA): the dQ kernel (which also writes the
 // per-query statistics the second kernel reads) then the dK/dV kernel, in
 // stream order.  workspace holds bwd_stats_bytes(BH, Nq) bytes.

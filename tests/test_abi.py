@@ -39,7 +39,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for want in ("fa_fwd", "fa_fwd_varlen", "fa_varlen_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_paged_decode", "fa_splitkv_workspace_bytes", "fa_status_string",
+    for want in ("fa_fwd", "fa_fwd_fp8", "fa_quantize_fp8", "fa_fp8_pack_bytes", "fa_fwd_varlen", "fa_varlen_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_paged_decode", "fa_splitkv_workspace_bytes", "fa_status_string",
                  "fa_last_error", "fa_release_workspace", "fa_default_num_splits", "fa_map_workgroup"):
         assert want in names
 
@@ -278,3 +278,52 @@ def test_varlen_workspace_bytes(fa):
     assert fa.fa_varlen_workspace_bytes(16, 70000) == ((2 + 2 * (547 + 16)) * 4 + 255) // 256 * 256
     assert fa.fa_varlen_workspace_bytes(0, 10) == 0 and fa.fa_varlen_workspace_bytes(9000, 10) == 0
     assert call_varlen(fa, ws_bytes=100) == 4
+
+
+FQ, FK, FV, FS, FP, FO, FL = (0x10000000 * i for i in range(30, 37))
+
+
+def call_quant(fa, pack_bytes=None, **over):
+    a = dict(q=FQ, k=FK, v=FV, signs=FS, B=2, H=4, Nq=300, Nk=500, d=128, dtype=2, pack=FP)
+    a.update(over)
+    if pack_bytes is None:
+        pack_bytes = fa.fa_fp8_pack_bytes(2, 4, 300, 500, 128)
+    return fa.lib.fa_quantize_fp8(a["q"], a["k"], a["v"], a["signs"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"],
+                                  a["dtype"], a["pack"], pack_bytes, None)
+
+
+def call_fwd_fp8(fa, **over):
+    a = dict(pack=FP, out=FO, lse=FL, B=2, H=4, Nq=300, Nk=500, d=128, scale=0.088, causal=1, dtype=2)
+    a.update(over)
+    return fa.lib.fa_fwd_fp8(a["pack"], a["out"], a["lse"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["scale"],
+                             a["causal"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), 1), (dict(pack=None), 1), (dict(B=0), 1), (dict(Nk=0), 1),
+    (dict(d=32), 2), (dict(d=96), 2), (dict(dtype=0), 2), (dict(q=FQ + 8), 2), (dict(pack=FP + 16), 2),
+    (dict(signs=FS + 2), 2), (dict(pack=FK), 1), (dict(pack=FQ + 256), 1),
+])
+def test_quantize_fp8_rejects_invalid_arguments(fa, over, code):
+    assert call_quant(fa, **over) == code
+    assert fa.fa_last_error() != ""
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(pack=None), 1), (dict(out=None), 1), (dict(H=0), 1), (dict(scale=0.0), 1), (dict(causal=5), 1),
+    (dict(d=32), 2), (dict(dtype=0), 2), (dict(pack=FP + 64), 2), (dict(out=FO + 8), 2), (dict(lse=FL + 1), 2),
+    (dict(out=FP + 1024), 1), (dict(lse=FO + 16), 1),
+])
+def test_fwd_fp8_rejects_invalid_arguments(fa, over, code):
+    assert call_fwd_fp8(fa, **over) == code
+    assert fa.fa_last_error() != ""
+
+
+def test_fp8_pack_bytes_follow_the_documented_layout(fa):
+    up = lambda x: (x + 255) // 256 * 256
+    B, H, Nq, Nk, d = 2, 4, 300, 500, 128
+    BH, Nkp = B * H, 512
+    want = up(BH * Nq * d) + up(BH * Nkp * d) + up(BH * d * Nkp) + 2 * up(3 * BH * 4)
+    assert fa.fa_fp8_pack_bytes(B, H, Nq, Nk, d) == want
+    assert fa.fa_fp8_pack_bytes(B, H, Nq, Nk, 32) == 0
+    assert call_quant(fa, pack_bytes=want - 1) == 4
