@@ -36,10 +36,35 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector (packed)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-KERNEL_SOURCES = ["io_aware_amd/csrc/fa_prefill.hip", "io_aware_amd/csrc/fa_layout.h",
-                  "io_aware_amd/csrc/fa_decode.hip", "io_aware_amd/csrc/fa_f32.hip",
-                  "io_aware_amd/csrc/fa_backward.hip", "io_aware_amd/csrc/fa_device.h",
-                  "io_aware_amd/csrc/fa_fp8.hip"]
+# the sources each workload's dominant kernel is built from (a committed
+# traffic record is used only while their hash is unchanged)
+_COMMON = ["io_aware_amd/csrc/fa_layout.h", "io_aware_amd/csrc/fa_device.h"]
+KERNEL_SOURCES = {
+    "prefill": ["io_aware_amd/csrc/fa_prefill.hip"] + _COMMON,
+    "f32": ["io_aware_amd/csrc/fa_f32.hip"],
+    "decode": ["io_aware_amd/csrc/fa_decode.hip"],
+    "backward": ["io_aware_amd/csrc/fa_backward.hip"] + _COMMON,
+    "fp8": ["io_aware_amd/csrc/fa_fp8.hip"] + _COMMON,
+}
+
+
+def workload_kernel(name: str):
+    """(source family, name pattern of the dominant kernel) of a workload."""
+    import fa_inputs
+    if name in fa_inputs.PAGED_WORKLOADS:
+        return "decode", "splitkv_partial"
+    if name in fa_inputs.VARLEN_WORKLOADS:
+        return "prefill", "prefill_kernel"
+    w = fa_inputs.WORKLOADS[name]
+    if w.fp8:
+        return "fp8", "fp8_fwd_kernel"
+    if w.backward:
+        return "backward", "bwd_dkdv_kernel"
+    if w.num_splits:
+        return "decode", "splitkv_partial"
+    if w.dtype == "f32":
+        return "f32", "prefill_f32"
+    return "prefill", "prefill_kernel"
 
 
 def workload_flops(w) -> float:
@@ -58,9 +83,9 @@ def workload_bytes(w) -> float:
     return float(es * w.B * w.H * (2 * w.Nq * w.d + 2 * w.Nk * w.d) + 4 * w.B * w.H * w.Nq)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(family: str) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -74,7 +99,7 @@ def measured_traffic(workload: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(workload_kernel(workload)[0]):
         return None
     return rec.get("hbm_bytes_per_launch")
 
