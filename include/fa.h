@@ -168,7 +168,7 @@ size_t fa_varlen_workspace_bytes(int num_seqs, int total_q);
  * device each sequence's bounds are clamped into [0, total] and the tile
  * list into its bound, so inconsistent offsets give wrong rows, never an
  * access outside the tensors or the workspace.  A query with no key gets O = 0 and
- * LSE = -inf.  1 <= num_seqs <= 8192.  A schedule kernel writes the tile
+ * LSE = -inf.  1 <= num_seqs <= 4096.  A schedule kernel writes the tile
  * list into ``workspace`` (at least fa_varlen_workspace_bytes(num_seqs,
  * total_q) bytes, 16-byte aligned), then the attention kernel runs over it.
  */

@@ -304,7 +304,7 @@ int fa_fwd_varlen(const void *q, const void *k, const void *v, void *out, float 
     if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
     if (dtype != FA_F16 && dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "the variable-length path takes fp16 or bf16");
     if (d != 32 && d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "d must be 32, 64 or 128");
-    if (num_seqs > fa::kMaxVarlenSeqs) return fail(FA_ERR_UNSUPPORTED, "num_seqs must be <= 8192");
+    if (num_seqs > fa::kMaxVarlenSeqs) return fail(FA_ERR_UNSUPPORTED, "num_seqs must be <= 4096");
     if ((int64_t)total_q * H * d > INT32_MAX || (int64_t)total_k * H * d > INT32_MAX)
         return fail(FA_ERR_UNSUPPORTED, "total_q*H*d and total_k*H*d must each fit in 31 bits");
     if ((int64_t)H * fa::varlen_max_tiles(num_seqs, total_q, 128) > INT32_MAX)

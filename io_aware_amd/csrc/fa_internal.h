@@ -33,7 +33,7 @@ hipError_t launch_prefill(int dtype, int d, bool causal, int shape,
 // k and v [total_k, H, d], out like q, lse [H, total_q]; cu_q, cu_k the
 // int32 offsets [S + 1] (device).  A schedule kernel first writes the tile
 // list into workspace (varlen_workspace_ints ints).
-constexpr int kMaxVarlenSeqs = 8192;
+constexpr int kMaxVarlenSeqs = 4096;
 long long varlen_max_tiles(int S, int total_q, int block_rows);
 hipError_t launch_prefill_varlen(int dtype, int d, bool causal, int shape, const void *q, const void *k,
                                  const void *v, void *out, float *lse, const int *cu_q, const int *cu_k, int S,

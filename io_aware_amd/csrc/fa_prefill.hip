@@ -379,10 +379,15 @@ void prefill_kernel(PrefillArgs a) {
 // Tile schedule of a packed variable-length batch ("9.4 FlashAttention 与
 // FlashMLA" section 9.4.6: the work of every workgroup is fixed before the
 // attention launch, cutting sequences of different lengths into equal
-// tiles).  One workgroup lists the (sequence, Q block) tiles of Br queries
-// and orders them by their number of K/V blocks, longest first, so the
-// attention grid starts the long tiles first and the short ones fill the
-// tail.  Output: sched[0] = number of tiles, then the pairs from index 2.
+// tiles).  One workgroup orders the sequences by length, longest first (a
+// counting sort on 1024 buckets), and lists each sequence's (sequence, Q
+// block) tiles of Br queries together, the longest (last, under the mask)
+// first.  The attention grid takes tile t for every head h as workgroup
+// t*H + h, so all tiles of one (sequence, head) run back to back on one XCD
+// (workgroups go to XCD wg % 8; with H a multiple of 8 that is h % 8) and
+// its K/V stay in that XCD's L2, while long work starts first and short
+// work fills the tail.  Output: sched[0] = number of tiles, then the pairs
+// from index 2.
 // ---------------------------------------------------------------------------
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedBuckets = 1024;
@@ -391,91 +396,95 @@ template <int BR, int BC, bool CAUSAL>
 __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(const int *cu_q, const int *cu_k, int S,
                                                                          int total_q, int total_k, int max_tiles,
                                                                          int *sched) {
-    __shared__ int tile_start[kMaxVarlenSeqs + 1];
+    __shared__ int order[kMaxVarlenSeqs];           // sequences, longest first
+    __shared__ int tile_start[kMaxVarlenSeqs + 1];  // first tile of order[i]
     __shared__ int hist[kSchedBuckets];
     __shared__ int scan[kSchedThreads];
-    __shared__ int wmax_s;
+    __shared__ int lmax_s;
     static_assert(kSchedBuckets == kSchedThreads, "one bucket per thread");
     const int tid = threadIdx.x;
-    if (tid == 0) wmax_s = 0;
-    hist[tid] = 0;
-    __syncthreads();
-
-    // Q tiles per sequence, their exclusive prefix sum, and the longest K/V
-    // block count (for the bucket scale)
-    int carry = 0;
-    for (int base = 0; base < S; base += kSchedThreads) {
-        const int s = base + tid;
-        int nb = 0;
-        if (s < S) {
-            int qs, qe, ks, ke;
-            layout::varlen_bounds(cu_q, s, total_q, qs, qe);
-            layout::varlen_bounds(cu_k, s, total_k, ks, ke);
-            nb = (qe - qs + BR - 1) / BR;
-            atomicMax(&wmax_s, (ke - ks + BC - 1) / BC);
-        }
-        scan[tid] = nb;
+    auto bounds = [&](int s, int &nb, int &work) {
+        int qs, qe, ks, ke;
+        layout::varlen_bounds(cu_q, s, total_q, qs, qe);
+        layout::varlen_bounds(cu_k, s, total_k, ks, ke);
+        nb = (qe - qs + BR - 1) / BR;
+        work = nb > 0 ? (ke - ks) : 0;  // key count orders the sequences
+    };
+    // inclusive block scan of one value per thread (every thread calls it)
+    auto block_scan = [&](int v) {
+        scan[tid] = v;
         __syncthreads();
         for (int off = 1; off < kSchedThreads; off <<= 1) {
-            const int v = tid >= off ? scan[tid - off] : 0;
+            const int x = tid >= off ? scan[tid - off] : 0;
             __syncthreads();
-            scan[tid] += v;
+            scan[tid] += x;
             __syncthreads();
         }
-        if (s < S) tile_start[s] = carry + scan[tid] - nb;
-        carry += scan[kSchedThreads - 1];
+        const int r = scan[tid];
+        const int total = scan[kSchedThreads - 1];
         __syncthreads();
+        return make_int2(r, total);
+    };
+
+    if (tid == 0) lmax_s = 0;
+    hist[tid] = 0;
+    __syncthreads();
+    for (int s = tid; s < S; s += kSchedThreads) {
+        int nb, work;
+        bounds(s, nb, work);
+        atomicMax(&lmax_s, work);
+    }
+    __syncthreads();
+    const int lmax = lmax_s;
+    auto bucket = [&](int work) {  // descending: the longest sequences in bucket 0
+        const int b = lmax > 0 ? (int)((long long)work * (kSchedBuckets - 1) / lmax) : 0;
+        return kSchedBuckets - 1 - b;
+    };
+    for (int s = tid; s < S; s += kSchedThreads) {
+        int nb, work;
+        bounds(s, nb, work);
+        atomicAdd(&hist[bucket(work)], 1);
+    }
+    __syncthreads();
+    {
+        const int own = hist[tid];
+        const int2 r = block_scan(own);
+        hist[tid] = r.x - own;  // first position of the bucket
+    }
+    __syncthreads();
+    for (int s = tid; s < S; s += kSchedThreads) {
+        int nb, work;
+        bounds(s, nb, work);
+        order[atomicAdd(&hist[bucket(work)], 1)] = s;
+    }
+    __syncthreads();
+    // first tile of each sequence in that order
+    int carry = 0;
+    for (int base = 0; base < S; base += kSchedThreads) {
+        const int i = base + tid;
+        int nb = 0, work;
+        if (i < S) bounds(order[i], nb, work);
+        const int2 r = block_scan(nb);
+        if (i < S) tile_start[i] = carry + r.x - nb;
+        carry += r.y;
     }
     const int T = carry;
     if (tid == 0) tile_start[S] = T;
     __syncthreads();
-    const int wmax = wmax_s;
-
-    // tile t -> (sequence, Q block) and its descending-work bucket
-    auto locate = [&](int t, int &s, int &qb) {
-        int lo = 0, hi = S - 1;  // the last sequence whose first tile is <= t (it has tiles)
+    for (int t = tid; t < T && t < max_tiles; t += kSchedThreads) {
+        int lo = 0, hi = S - 1;  // the last position whose first tile is <= t (it has tiles)
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (tile_start[mid] <= t) lo = mid;
             else hi = mid - 1;
         }
-        s = lo;
-        qb = t - tile_start[lo];
-        int qs, qe, ks, ke;
-        layout::varlen_bounds(cu_q, s, total_q, qs, qe);
-        layout::varlen_bounds(cu_k, s, total_k, ks, ke);
-        const int nk = ke - ks;
-        const int kv_end = CAUSAL ? min(nk, (qb + 1) * BR) : nk;
-        const int work = (kv_end + BC - 1) / BC;
-        const int b = wmax > 0 ? (int)((long long)work * (kSchedBuckets - 1) / wmax) : 0;
-        return kSchedBuckets - 1 - b;
-    };
-    for (int t = tid; t < T; t += kSchedThreads) {
-        int s, qb;
-        atomicAdd(&hist[locate(t, s, qb)], 1);
+        const int s = order[lo];
+        const int r = t - tile_start[lo];
+        const int nb = tile_start[lo + 1] - tile_start[lo];
+        sched[2 + 2 * t] = s;
+        sched[3 + 2 * t] = CAUSAL ? nb - 1 - r : r;  // under the mask the last Q block is the longest
     }
-    __syncthreads();
-    // exclusive prefix sum of the bucket sizes
-    const int own = hist[tid];
-    scan[tid] = own;
-    __syncthreads();
-    for (int off = 1; off < kSchedThreads; off <<= 1) {
-        const int v = tid >= off ? scan[tid - off] : 0;
-        __syncthreads();
-        scan[tid] += v;
-        __syncthreads();
-    }
-    hist[tid] = scan[tid] - own;
-    __syncthreads();
-    for (int t = tid; t < T; t += kSchedThreads) {
-        int s, qb;
-        const int pos = atomicAdd(&hist[locate(t, s, qb)], 1);
-        if (pos < max_tiles) {  // only offsets that decrease (overlapping sequences) can exceed the bound
-            sched[2 + 2 * pos] = s;
-            sched[3 + 2 * pos] = qb;
-        }
-    }
-    if (tid == 0) sched[0] = T < max_tiles ? T : max_tiles;
+    if (tid == 0) sched[0] = T < max_tiles ? T : max_tiles;  // only decreasing offsets can exceed the bound
 }
 
 template <typename T, int D, bool CAUSAL, int NW, int QW, int OCC, int BC = 64>

@@ -253,7 +253,7 @@ def call_varlen(fa, ws_bytes=None, **over):
     a = dict(VGOOD)
     a.update(over)
     if ws_bytes is None:
-        ws_bytes = fa.fa_varlen_workspace_bytes(max(1, min(a["S"], 8192)), max(1, a["total_q"]))
+        ws_bytes = fa.fa_varlen_workspace_bytes(max(1, min(a["S"], 4096)), max(1, a["total_q"]))
     return fa.lib.fa_fwd_varlen(a["q"], a["k"], a["v"], a["out"], a["lse"], a["cq"], a["ck"], a["S"],
                                 a["total_q"], a["total_k"], a["H"], a["d"], a["scale"], a["causal"], a["dtype"],
                                 a["ws"], ws_bytes, None)
@@ -262,7 +262,7 @@ def call_varlen(fa, ws_bytes=None, **over):
 @pytest.mark.parametrize("over,code", [
     (dict(q=None), 1), (dict(cq=None), 1), (dict(ck=None), 1), (dict(out=None), 1), (dict(S=0), 1),
     (dict(total_q=0), 1), (dict(total_k=0), 1), (dict(H=0), 1), (dict(scale=-1.0), 1), (dict(causal=2), 1),
-    (dict(dtype=0), 2), (dict(d=80), 2), (dict(S=8193), 2), (dict(total_q=1 << 25), 2),
+    (dict(dtype=0), 2), (dict(d=80), 2), (dict(S=4097), 2), (dict(total_q=1 << 25), 2),
     (dict(q=VQ + 8), 2), (dict(cq=VCQ + 2), 2), (dict(lse=VL + 1), 2),
     (dict(out=VK + 64), 1), (dict(lse=VCQ), 1), (dict(lse=VO + 16), 1),
     (dict(ws=None), 4), (dict(ws=VW + 4), 4), (dict(ws=VO), 4), (dict(ws=VCK), 4),
@@ -276,7 +276,7 @@ def test_varlen_workspace_bytes(fa):
     # 4 * (2 + 2 * (ceil(1000 / 128) + 4)) = 104 -> 256
     assert fa.fa_varlen_workspace_bytes(4, 1000) == 256
     assert fa.fa_varlen_workspace_bytes(16, 70000) == ((2 + 2 * (547 + 16)) * 4 + 255) // 256 * 256
-    assert fa.fa_varlen_workspace_bytes(0, 10) == 0 and fa.fa_varlen_workspace_bytes(9000, 10) == 0
+    assert fa.fa_varlen_workspace_bytes(0, 10) == 0 and fa.fa_varlen_workspace_bytes(4097, 10) == 0
     assert call_varlen(fa, ws_bytes=100) == 4
 
 
