@@ -50,6 +50,10 @@ constexpr float kE4M3Max = 448.0f;
 __device__ __forceinline__ f32x16 mfma_e4m3(i32x8 a, i32x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
+// D (16x16 float32) += A (16x128) B (128x16), A and B E4M3 (32 codes per lane)
+__device__ __forceinline__ f32x4 mfma16_e4m3(i32x8 a, i32x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
 constexpr int kKeyGroup = 64;   // keys per attention tile and per V^T group
 
 struct Fp8Pack {
@@ -403,11 +407,24 @@ void fp8_fwd_kernel(Fp8Args a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
     // two running sums: l_part of the float32 P (for LSE and the lazy-
-    // rescale bound) and l8_part of the E4M3-rounded P that enters P V (so O
-    // is normalised by the weights it was formed with)
+    // rescale bound) and l8 of the E4M3-rounded P that enters P V (so O is
+    // normalised by the weights it was formed with).  l8 is summed on the
+    // matrix core: read as the B operand of the 16x16x128 product, the P
+    // registers of lanes n and n+32 (query n) form k-quarters 0 and 2 of
+    // column n, those of lanes n+16 and n+48 (query n+16) k-quarters 1 and
+    // 3.  With A row 0 = ones on quarters 0, 2 and row 1 = ones on quarters
+    // 1, 3 (lanes 0, 32 and 17, 49; every other lane zero), lane n < 16 of
+    // the accumulator holds the sum of query n in register 0 and of query
+    // n+16 in register 1, whatever the byte order inside a lane.
     float m_held = -__builtin_inff();
     float l_part = 0.0f;
-    float l8_part = 0.0f;
+    f32x4 l8acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    i32x8 ones8;
+    {
+        const int ones = (lane == 0 || lane == 32 || lane == 17 || lane == 49) ? 0x38383838 : 0;  // E4M3 1.0
+#pragma unroll
+        for (int w = 0; w < 8; ++w) ones8[w] = ones;
+    }
 
     const int kv_end = CAUSAL ? min(Nk, q0 + BR) : Nk;
     const int nt = (kv_end + BC - 1) / BC;
@@ -442,10 +459,8 @@ void fp8_fwd_kernel(Fp8Args a) {
         }
         // ---- online softmax with the lazy rescale; P to E4M3 -------------------
         i32x8 pf;
-        float l8sum = 0.0f;
         auto exp_tile = [&](float msub) {
             float lsum = 0.0f;
-            l8sum = 0.0f;
 #pragma unroll
             for (int w = 0; w < 8; ++w) {  // dword w: slots 4w .. 4w+3 = (kb, r) = (w / 4, 4 (w % 4) + e)
                 float t[4];
@@ -455,9 +470,6 @@ void fp8_fwd_kernel(Fp8Args a) {
                     lsum += t[e];
                 }
                 pf[w] = (int)to_e4m3x4(t[0], t[1], t[2], t[3]);
-                const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(pf[w], false);
-                const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(pf[w], true);
-                l8sum += (lo[0] + lo[1]) + (hi[0] + hi[1]);
             }
             return lsum;
         };
@@ -478,13 +490,16 @@ void fp8_fwd_kernel(Fp8Args a) {
             const float alpha = (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_held - m_new);
             m_held = m_new;
             l_part *= alpha;
-            l8_part *= alpha;
+            // lane n < 16 keeps queries n (register 0) and n + 16 (register 1)
+            const float alpha_hi = __shfl(alpha, (lane + 16) & 63);
+            l8acc[0] *= alpha;
+            l8acc[1] *= alpha_hi;
 #pragma unroll
             for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
             lsum = exp_tile((m_new == -__builtin_inff()) ? 0.0f : m_new);
         }
         l_part += lsum;
-        l8_part += l8sum;
+        l8acc = mfma16_e4m3(ones8, pf, l8acc);
         // ---- O^T += V^T P^T -------------------------------------------------------
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
@@ -517,7 +532,9 @@ void fp8_fwd_kernel(Fp8Args a) {
 
     // ---- epilogue: O = acc * descale_v / l, LSE = (m + log2 l) ln 2 ------------
     const float l = xor32_sum(l_part);
-    const float l8 = xor32_sum(l8_part);
+    const float l8_lo = __shfl(l8acc[0], l32 & 15);
+    const float l8_hi = __shfl(l8acc[1], l32 & 15);
+    const float l8 = (l32 < 16) ? l8_lo : l8_hi;
     if (row < Nq) {
         OutT *op = static_cast<OutT *>(a.out) + ((size_t)bh * Nq + row) * D;
         const float f = (l8 > 0.0f) ? dv / l8 : 0.0f;
