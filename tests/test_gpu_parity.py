@@ -118,6 +118,20 @@ def test_every_prefill_tile_shape(fa, shape_id, monkeypatch):
                      label="shape %d d%d causal=%d" % (shape_id, d, causal))
 
 
+@pytest.mark.parametrize("shape_id", [0, 3])
+def test_prefill_shape_edge_cases(fa, shape_id, monkeypatch):
+    """Key counts below, at and above the query count, single keys and
+    queries, partial blocks of queries and keys, at d = 128 for the 64-key
+    tile shape and the default 32-key tile shape."""
+    monkeypatch.setenv("FA_PREFILL_SHAPE", str(shape_id))
+    cases = [(1, 2, 300, 1000), (1, 2, 1000, 300), (2, 1, 257, 31), (1, 1, 64, 1), (1, 1, 1, 33),
+             (1, 1, 512, 512), (1, 1, 33, 2000)]
+    for i, (B, H, Nq, Nk) in enumerate(cases):
+        for causal in (False, True):
+            run_full(fa, B, H, Nq, Nk, 128, "bf16", causal, seed=900 + i, q_sigma=2.0,
+                     label="shape %d B%d H%d Nq%d Nk%d causal=%d" % (shape_id, B, H, Nq, Nk, causal))
+
+
 def test_triton_page_regression(fa):
     """The fp16 shapes and seed of the Triton page's test; its bound is
     max-abs < 1e-3 against an fp16 torch reference, here against fp64."""
