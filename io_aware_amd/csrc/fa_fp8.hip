@@ -65,12 +65,35 @@ struct Fp8Pack {
 };
 
 template <typename T>
-__device__ __forceinline__ void load8(const T *p, float x[8]) {
-    const u32x4 raw = *reinterpret_cast<const u32x4 *>(p);
+__device__ __forceinline__ void unpack8(u32x4 raw, float x[8]) {
     typedef T t8 __attribute__((ext_vector_type(8)));
     const t8 v = __builtin_bit_cast(t8, raw);
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
+}
+
+// 16 bytes of a row that is read once (nontemporal), or zeros
+template <typename T>
+__device__ __forceinline__ u32x4 load_once(const T *p, bool ok) {
+    return ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p)) : u32x4{0u, 0u, 0u, 0u};
+}
+
+// The value of lane ^ M within each row of 16 lanes, by DPP (vector ALU,
+// no LDS traffic): quad permutations for M = 1, 2; a rotation by 8 for
+// M = 8; for M = 4 a rotation by 12 (lanes with bit 2 clear) or by 4
+// (set), chosen per lane.
+template <int M>
+__device__ __forceinline__ float row_xor(float v, int lane) {
+    const int b = __float_as_int(v);
+    if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, true));
+    if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, true));
+    if constexpr (M == 8) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x128, 0xF, 0xF, true));
+    if constexpr (M == 4) {
+        const int up = __builtin_amdgcn_mov_dpp(b, 0x12C, 0xF, 0xF, true);    // lane i <- i + 4
+        const int down = __builtin_amdgcn_mov_dpp(b, 0x124, 0xF, 0xF, true);  // lane i <- i - 4
+        return __int_as_float((lane & 4) ? down : up);
+    }
+    return v;
 }
 
 // (x * signs) H_d / sqrt(d) (nothing if signs is null) for the row a group of CH = D/8 lanes holds
@@ -95,15 +118,22 @@ __device__ __forceinline__ void transform_row(float x[8], const float *signs, in
             }
         }
     }
+    static_assert(CH <= 16, "a row spans at most one 16-lane DPP row");
+    auto stage = [&](auto m_tag) {
+        constexpr int M = decltype(m_tag)::value;
+        if constexpr (M < CH) {
+            // lower lane: x + other; upper lane: other - x.  Both are
+            // fma(x, +-1, other): x * (+-1) is exact, so the one rounding is
+            // that of the sum, as in a + b and a - b.
+            const float sgn = (lc & M) != 0 ? -1.0f : 1.0f;
 #pragma unroll
-    for (int m = 1; m < CH; m <<= 1) {
-        const bool upper = (lc & m) != 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float other = __shfl_xor(x[e], m);
-            x[e] = upper ? other - x[e] : x[e] + other;
+            for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(x[e], sgn, row_xor<M>(x[e], lc));
         }
-    }
+    };
+    stage(Int<1>{});
+    stage(Int<2>{});
+    stage(Int<4>{});
+    stage(Int<8>{});
     const float norm = (float)(1.0 / __builtin_sqrt((double)D));  // 1/sqrt(d) rounded once to float32
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] *= norm;
@@ -142,22 +172,33 @@ __global__ __launch_bounds__(kQuantThreads) void fp8_amax_kernel(QuantArgs a) {
     const int r0 = blockIdx.y * kQuantRows;
     const int tid = threadIdx.x;
     const int lc = tid % CH;
+    constexpr int NP = kQuantRows / RPI;      // passes
     float m[3] = {0.0f, 0.0f, 0.0f};
-    for (int pass = 0; pass < kQuantRows / RPI; ++pass) {
+    // every pass's loads are issued before any is used
+    u32x4 rq[NP], rk[NP], rv[NP];
+#pragma unroll
+    for (int pass = 0; pass < NP; ++pass) {
+        const int row = r0 + pass * RPI + tid / CH;
+        rq[pass] = load_once(static_cast<const T *>(a.q) + ((size_t)bh * a.Nq + row) * D + 8 * lc, row < a.Nq);
+        rk[pass] = load_once(static_cast<const T *>(a.k) + ((size_t)bh * a.Nk + row) * D + 8 * lc, row < a.Nk);
+        rv[pass] = load_once(static_cast<const T *>(a.v) + ((size_t)bh * a.Nk + row) * D + 8 * lc, row < a.Nk);
+    }
+#pragma unroll
+    for (int pass = 0; pass < NP; ++pass) {
         const int row = r0 + pass * RPI + tid / CH;
         float x[8];
-        if (row < a.Nq) {  // CH lanes share the row: the group is uniform, the shuffles stay inside it
-            load8(static_cast<const T *>(a.q) + ((size_t)bh * a.Nq + row) * D + 8 * lc, x);
+        if (row < a.Nq) {  // CH lanes share the row: the group is uniform, the exchanges stay inside it
+            unpack8<T>(rq[pass], x);
             transform_row<D>(x, a.signs, lc);
 #pragma unroll
             for (int e = 0; e < 8; ++e) m[0] = __builtin_fmaxf(m[0], __builtin_fabsf(x[e]));
         }
         if (row < a.Nk) {
-            load8(static_cast<const T *>(a.k) + ((size_t)bh * a.Nk + row) * D + 8 * lc, x);
+            unpack8<T>(rk[pass], x);
             transform_row<D>(x, a.signs, lc);
 #pragma unroll
             for (int e = 0; e < 8; ++e) m[1] = __builtin_fmaxf(m[1], __builtin_fabsf(x[e]));
-            load8(static_cast<const T *>(a.v) + ((size_t)bh * a.Nk + row) * D + 8 * lc, x);
+            unpack8<T>(rv[pass], x);
 #pragma unroll
             for (int e = 0; e < 8; ++e) m[2] = __builtin_fmaxf(m[2], __builtin_fabsf(x[e]));
         }
@@ -204,12 +245,23 @@ __global__ __launch_bounds__(kQuantThreads) void fp8_quantize_kernel(QuantArgs a
         const float amax = __uint_as_float(a.pack.amax[tid * a.BH + bh]);
         a.pack.descale[tid * a.BH + bh] = amax > 0.0f ? amax / kE4M3Max : 1.0f;
     }
-    for (int pass = 0; pass < kQuantRows / RPI; ++pass) {
+    constexpr int NP = kQuantRows / RPI;      // passes
+    // every pass's loads are issued before any is used
+    u32x4 rq[NP], rk[NP], rv[NP];
+#pragma unroll
+    for (int pass = 0; pass < NP; ++pass) {
+        const int row = r0 + pass * RPI + tid / CH;
+        rq[pass] = load_once(static_cast<const T *>(a.q) + ((size_t)bh * a.Nq + row) * D + 8 * lc, row < a.Nq);
+        rk[pass] = load_once(static_cast<const T *>(a.k) + ((size_t)bh * a.Nk + row) * D + 8 * lc, row < a.Nk);
+        rv[pass] = load_once(static_cast<const T *>(a.v) + ((size_t)bh * a.Nk + row) * D + 8 * lc, row < a.Nk);
+    }
+#pragma unroll
+    for (int pass = 0; pass < NP; ++pass) {
         const int rl = pass * RPI + tid / CH;
         const int row = r0 + rl;
         float x[8];
         if (row < a.Nq) {
-            load8(static_cast<const T *>(a.q) + ((size_t)bh * a.Nq + row) * D + 8 * lc, x);
+            unpack8<T>(rq[pass], x);
             transform_row<D>(x, a.signs, lc);
             u32x2 c;
             c[0] = to_e4m3x4(clamp448(x[0] * iq), clamp448(x[1] * iq), clamp448(x[2] * iq), clamp448(x[3] * iq));
@@ -219,11 +271,11 @@ __global__ __launch_bounds__(kQuantThreads) void fp8_quantize_kernel(QuantArgs a
         if (row < a.Nkp) {  // key rows past Nk (padding up to the group) are zero codes
             u32x2 c = {0u, 0u}, cv = {0u, 0u};
             if (row < a.Nk) {
-                load8(static_cast<const T *>(a.k) + ((size_t)bh * a.Nk + row) * D + 8 * lc, x);
+                unpack8<T>(rk[pass], x);
                 transform_row<D>(x, a.signs, lc);
                 c[0] = to_e4m3x4(clamp448(x[0] * ik), clamp448(x[1] * ik), clamp448(x[2] * ik), clamp448(x[3] * ik));
                 c[1] = to_e4m3x4(clamp448(x[4] * ik), clamp448(x[5] * ik), clamp448(x[6] * ik), clamp448(x[7] * ik));
-                load8(static_cast<const T *>(a.v) + ((size_t)bh * a.Nk + row) * D + 8 * lc, x);
+                unpack8<T>(rv[pass], x);
                 cv[0] = to_e4m3x4(clamp448(x[0] * iv), clamp448(x[1] * iv), clamp448(x[2] * iv), clamp448(x[3] * iv));
                 cv[1] = to_e4m3x4(clamp448(x[4] * iv), clamp448(x[5] * iv), clamp448(x[6] * iv), clamp448(x[7] * iv));
             }
