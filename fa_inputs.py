@@ -255,6 +255,24 @@ def make_qkv(B: int, H: int, Nq: int, Nk: int, d: int, dtype, seed: int,
     return q.to(dtype), k.to(dtype), v.to(dtype)
 
 
+def make_qkv_device(B: int, H: int, Nq: int, Nk: int, d: int, dtype, seed: int, device):
+    """Like make_qkv, but drawn on ``device`` by its own seeded generator
+    (for tensors too large to draw on the host): q [B,H,Nq,d], k and v
+    [B,H,Nk,d] standard normal in float32, rounded to ``dtype``, one head
+    at a time so the float32 draw never exceeds one head."""
+    if isinstance(dtype, str):
+        dtype = DTYPES[dtype]
+    g = torch.Generator(device=device).manual_seed(int(seed))
+    out = []
+    for n in (Nq, Nk, Nk):
+        t = torch.empty((B, H, n, d), dtype=dtype, device=device)
+        flat = t.view(B * H, n, d)
+        for i in range(B * H):
+            flat[i].copy_(torch.randn((n, d), generator=g, dtype=torch.float32, device=device))
+        out.append(t)
+    return tuple(out)
+
+
 def make_workload(w: Workload):
     return make_qkv(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.seed, w.q_sigma)
 
