@@ -2,14 +2,19 @@
 //
 // Same method as the 16-bit path ("6. FlashAttention 分块逻辑" sections 3-6;
 // "9.4 FlashAttention 与 FlashMLA" section 9.4.5) with Br = Bc = 64: a
-// workgroup of one wave owns 64 query rows (one per lane) of one
-// (batch, head); each lane keeps its query row, its float32 output row and
-// its running max / running sum in registers.  K/V blocks of 64 keys are
-// staged in LDS and read by all lanes at the same address (broadcast).  Per
-// block: scores, block max, one exact rescale of the row by exp(m - m_new),
-// P = exp(S - m_new), l += sum P, O += P V; after the last block O = O / l and
-// LSE = m + ln l.  Every product and sum is a float32 FMA; exp is exp2 with
-// scale*log2(e) folded in.
+// workgroup owns 64 query rows of one (batch, head), one row per lane of
+// each of its NW waves.  K/V blocks of 64 keys are staged in LDS by the whole
+// workgroup and read by all lanes of a wave at the same address
+// (broadcast); wave w takes keys w*64/NW .. (w+1)*64/NW - 1 of every block,
+// so the NW waves split the key loop.  Each lane keeps its query row, its
+// float32 output row and its running max / running sum over its wave's keys
+// in registers.  Per block: scores, block max, one exact rescale by
+// exp(m - m_new), P = exp(S - m_new), l += sum P, O += P V.  At the end the
+// NW partial states of a row are merged pairwise through LDS (the split-KV
+// combine of section 11 of the first page, inside one workgroup): with
+// M = max(m1, m2), l = l1 e^(m1-M) + l2 e^(m2-M), o likewise; then O = o / l
+// and LSE = M + ln l.  Every product and sum is a float32 FMA; exp is exp2
+// with scale*log2(e) folded in.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,18 +39,31 @@ struct F32Args {
     float scale_log2;
 };
 
+// waves per workgroup: as many as keep q and o (2 D floats per lane) in
+// registers at two or more waves per SIMD
+template <int D>
+constexpr int f32_waves() { return D <= 32 ? 16 : (D <= 64 ? 8 : 4); }
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(64) void prefill_f32_kernel(F32Args a) {
+__global__ __launch_bounds__(f32_waves<D>() * 64) void prefill_f32_kernel(F32Args a) {
+    constexpr int NW = f32_waves<D>();
     constexpr int BR = 64;
     constexpr int BC = 64;
-    constexpr int C4 = D / 4;  // float4 chunks per row
-    __shared__ f32x4 ks[BC * C4];
-    __shared__ f32x4 vs[BC * C4];
+    constexpr int KPW = BC / NW;  // keys of a block per wave
+    constexpr int C4 = D / 4;     // float4 chunks per row
+    constexpr int KV_FLOATS = 2 * BC * D;                 // one K and one V block
+    constexpr int MERGE_FLOATS = (NW / 2) * 64 * (D + 2);  // the upper half's (m, l, o) of a merge round
+    constexpr int SMEM_FLOATS = KV_FLOATS > MERGE_FLOATS ? KV_FLOATS : MERGE_FLOATS;
+    __shared__ __attribute__((aligned(16))) float smem[SMEM_FLOATS];
+    f32x4 *ks = reinterpret_cast<f32x4 *>(smem);
+    f32x4 *vs = ks + BC * C4;
 
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int bh = blockIdx.x / a.Tr;
     const int q0 = (blockIdx.x - bh * a.Tr) * BR;
-    const int row = q0 + tid;
+    const int row = q0 + lane;
     const int Nq = a.Nq;
     const int Nk = a.Nk;
     const float c = a.scale_log2;
@@ -65,13 +83,13 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(F32Args a) {
         q[t + 3] = x[3];
         o[t] = o[t + 1] = o[t + 2] = o[t + 3] = 0.f;
     }
-    float m = -__builtin_inff();
+    float m = -__builtin_inff();  // exp2 domain, over this wave's keys
     float l = 0.f;
 
     const int kv_end = CAUSAL ? min(Nk, q0 + BR) : Nk;
     for (int k0 = 0; k0 < kv_end; k0 += BC) {
         __syncthreads();  // the previous block's reads are done
-        for (int idx = tid; idx < BC * C4; idx += BR) {
+        for (int idx = tid; idx < BC * C4; idx += NW * 64) {
             const int key = k0 + idx / C4;
             const int c4 = idx % C4;
             f32x4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
@@ -84,10 +102,11 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(F32Args a) {
         }
         __syncthreads();
 
-        float s[BC];
+        float s[KPW];
         float mx = -__builtin_inff();
 #pragma unroll
-        for (int j = 0; j < BC; ++j) {
+        for (int jj = 0; jj < KPW; ++jj) {
+            const int j = wave * KPW + jj;
             float dot = 0.f;
 #pragma unroll
             for (int t = 0; t < C4; ++t) {
@@ -99,8 +118,8 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(F32Args a) {
             }
             const int key = k0 + j;
             const bool visible = key < Nk && (!CAUSAL || key <= row);
-            s[j] = visible ? dot : -__builtin_inff();
-            mx = __builtin_fmaxf(mx, s[j]);
+            s[jj] = visible ? dot : -__builtin_inff();
+            mx = __builtin_fmaxf(mx, s[jj]);
         }
         const float m_new = __builtin_fmaxf(m, mx * c);
         const float alpha = (m_new == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
@@ -109,8 +128,9 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(F32Args a) {
 #pragma unroll
         for (int t = 0; t < D; ++t) o[t] *= alpha;
 #pragma unroll
-        for (int j = 0; j < BC; ++j) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c, -msub));
+        for (int jj = 0; jj < KPW; ++jj) {
+            const int j = wave * KPW + jj;
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jj], c, -msub));
             l += p;
 #pragma unroll
             for (int t = 0; t < C4; ++t) {
@@ -124,7 +144,33 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(F32Args a) {
         m = m_new;
     }
 
-    if (row < Nq) {
+    // ---- merge the NW partial states of each row, halving the waves per round
+#pragma unroll
+    for (int half = NW / 2; half >= 1; half >>= 1) {
+        __syncthreads();  // LDS is free (block reads or the previous round are done)
+        if (wave >= half && wave < 2 * half) {
+            float *dst = smem + (size_t)((wave - half) * 64 + lane) * (D + 2);
+            dst[0] = m;
+            dst[1] = l;
+#pragma unroll
+            for (int t = 0; t < D; ++t) dst[2 + t] = o[t];
+        }
+        __syncthreads();
+        if (wave < half) {
+            const float *src = smem + (size_t)(wave * 64 + lane) * (D + 2);
+            const float m2 = src[0], l2 = src[1];
+            const float M = __builtin_fmaxf(m, m2);
+            // exp2(-inf) = 0 weighs out a side without keys; M = -inf: both empty
+            const float a1 = (M == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(m - M);
+            const float a2 = (M == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
+            l = __builtin_fmaf(l2, a2, l * a1);
+#pragma unroll
+            for (int t = 0; t < D; ++t) o[t] = __builtin_fmaf(src[2 + t], a2, o[t] * a1);
+            m = M;
+        }
+    }
+
+    if (wave == 0 && row < Nq) {
         const float inv = (l > 0.f) ? 1.f / l : 0.f;
         float *op = a.out + (size_t)bh * Nq * D + (size_t)row * D;
 #pragma unroll
@@ -150,7 +196,7 @@ hipError_t launch_f32_one(const void *q, const void *k, const void *v, void *out
     a.scale_log2 = sl;
     const long long nwg = (long long)BH * a.Tr;
     if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((prefill_f32_kernel<D, CAUSAL>), dim3((unsigned)nwg), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((prefill_f32_kernel<D, CAUSAL>), dim3((unsigned)nwg), dim3(f32_waves<D>() * 64), 0, stream, a);
     return hipGetLastError();
 }
 
