@@ -78,35 +78,46 @@ __device__ __forceinline__ u32x4 load_once(const T *p, bool ok) {
     return ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p)) : u32x4{0u, 0u, 0u, 0u};
 }
 
-// The value of lane ^ M within each row of 16 lanes, by DPP (vector ALU,
-// no LDS traffic): quad permutations for M = 1, 2; a rotation by 8 for
-// M = 8; for M = 4 a rotation by 12 (lanes with bit 2 clear) or by 4
-// (set), chosen per lane.
-template <int M>
-__device__ __forceinline__ float row_xor(float v, int lane) {
+// Lanes and chunks of a row.  A row of D elements is spread over CH = D/8
+// lanes of one DPP row (16 lanes), 8 consecutive elements (a 16-byte chunk)
+// per lane.  Lane L of the group holds chunk ck(L) = L ^ (L & 4 ? 3 : 0):
+// chunk bit k then sits across the lane exchange L ^ v_k with
+// v = (1, 2, 7, 8), and every v_k is one DPP move -- quad permutations for 1
+// and 2, the half-row mirror for 7, a row rotation by 8 for 8.
+__device__ __forceinline__ int chunk_of_lane(int lc) { return lc ^ ((lc & 4) ? 3 : 0); }
+
+// the value of lane ^ V within each row of 16 lanes
+template <int V>
+__device__ __forceinline__ float lane_xor(float v) {
     const int b = __float_as_int(v);
-    if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, true));
-    if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, true));
-    if constexpr (M == 8) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x128, 0xF, 0xF, true));
-    if constexpr (M == 4) {
-        const int up = __builtin_amdgcn_mov_dpp(b, 0x12C, 0xF, 0xF, true);    // lane i <- i + 4
-        const int down = __builtin_amdgcn_mov_dpp(b, 0x124, 0xF, 0xF, true);  // lane i <- i - 4
-        return __int_as_float((lane & 4) ? down : up);
-    }
-    return v;
+    constexpr int ctrl = V == 1 ? 0xB1 : V == 2 ? 0x4E : V == 7 ? 0x141 : 0x128;
+    static_assert(V == 1 || V == 2 || V == 7 || V == 8, "one DPP move per exchange");
+    return __int_as_float(__builtin_amdgcn_mov_dpp(b, ctrl, 0xF, 0xF, true));
 }
 
-// (x * signs) H_d / sqrt(d) (nothing if signs is null) for the row a group of CH = D/8 lanes holds
-// (lane lc of the group: elements 8*lc .. 8*lc+7).  The butterfly pairs
-// element i with i ^ h; the element with bit h clear becomes a + b, the one
-// with it set a - b (a the clear one), stage h = 1, 2, 4 in registers, then
-// h = 8, 16, ... across lanes.
-template <int D>
-__device__ __forceinline__ void transform_row(float x[8], const float *signs, int lc) {
-    constexpr int CH = D / 8;
-    if (signs == nullptr) return;  // no transform (M = I)
+// The sign flips of the transform for this lane's chunk, as XOR masks on the
+// packed 16-bit elements (bit 15 / 31 of each word): x * (+-1) is exact, so
+// flipping the sign bits of the inputs is the same as multiplying.
+__device__ __forceinline__ u32x4 sign_masks(const float *signs, int ck) {
+    u32x4 m = {0u, 0u, 0u, 0u};
+    if (signs != nullptr) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] *= signs[8 * lc + e];
+        for (int w = 0; w < 4; ++w)
+            m[w] = (signs[8 * ck + 2 * w] < 0.0f ? 0x8000u : 0u) | (signs[8 * ck + 2 * w + 1] < 0.0f ? 0x80000000u : 0u);
+    }
+    return m;
+}
+
+// H_d / sqrt(d) (with NORM; without it the unnormalised butterfly) of the
+// row a group of CH = D/8 lanes holds, the signs already applied (nothing if
+// there are no signs: M = I).  The butterfly pairs element i with i ^ h; the
+// element with bit h clear becomes a + b, the one with it set a - b (a the
+// clear one); stages h = 1, 2, 4 run in registers, h = 8, 16, 32, 64 across
+// the lanes of the group.
+template <int D, bool NORM>
+__device__ __forceinline__ void transform_row(float x[8], bool has_signs, int ck) {
+    constexpr int CH = D / 8;
+    if (!has_signs) return;  // no transform (M = I)
 #pragma unroll
     for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll
@@ -119,24 +130,27 @@ __device__ __forceinline__ void transform_row(float x[8], const float *signs, in
         }
     }
     static_assert(CH <= 16, "a row spans at most one 16-lane DPP row");
-    auto stage = [&](auto m_tag) {
-        constexpr int M = decltype(m_tag)::value;
-        if constexpr (M < CH) {
-            // lower lane: x + other; upper lane: other - x.  Both are
+    auto stage = [&](auto k_tag, auto v_tag) {
+        constexpr int K = decltype(k_tag)::value;
+        constexpr int V = decltype(v_tag)::value;
+        if constexpr ((1 << K) < CH) {
+            // lower chunk: x + other; upper chunk: other - x.  Both are
             // fma(x, +-1, other): x * (+-1) is exact, so the one rounding is
             // that of the sum, as in a + b and a - b.
-            const float sgn = (lc & M) != 0 ? -1.0f : 1.0f;
+            const float sgn = ((ck >> K) & 1) ? -1.0f : 1.0f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(x[e], sgn, row_xor<M>(x[e], lc));
+            for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(x[e], sgn, lane_xor<V>(x[e]));
         }
     };
-    stage(Int<1>{});
-    stage(Int<2>{});
-    stage(Int<4>{});
-    stage(Int<8>{});
-    const float norm = (float)(1.0 / __builtin_sqrt((double)D));  // 1/sqrt(d) rounded once to float32
+    stage(Int<0>{}, Int<1>{});
+    stage(Int<1>{}, Int<2>{});
+    stage(Int<2>{}, Int<7>{});
+    stage(Int<3>{}, Int<8>{});
+    if constexpr (NORM) {
+        const float norm = (float)(1.0 / __builtin_sqrt((double)D));  // 1/sqrt(d) rounded once to float32
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] *= norm;
+        for (int e = 0; e < 8; ++e) x[e] *= norm;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -151,6 +165,9 @@ __global__ void fp8_clear_kernel(uint32_t *p, int n) {
 // rows, 64 key rows and the 64 value rows of one key group.
 constexpr int kQuantRows = 64;
 constexpr int kQuantThreads = 256;
+// row blocks per amax workgroup: its waves reduce through LDS and it issues
+// one atomic per tensor, so each (head, tensor) word sees few atomics
+constexpr int kAmaxBlocks = 4;
 
 struct QuantArgs {
     const void *q;
@@ -168,47 +185,67 @@ template <typename T, int D>
 __global__ __launch_bounds__(kQuantThreads) void fp8_amax_kernel(QuantArgs a) {
     constexpr int CH = D / 8;
     constexpr int RPI = kQuantThreads / CH;   // rows per pass
+    constexpr int NP = kQuantRows / RPI;      // passes per row block
+    __shared__ float wmax[kQuantThreads / 64][3];
     const int bh = blockIdx.x;
-    const int r0 = blockIdx.y * kQuantRows;
     const int tid = threadIdx.x;
-    const int lc = tid % CH;
-    constexpr int NP = kQuantRows / RPI;      // passes
+    const int ck = chunk_of_lane(tid % CH);
+    const bool has_signs = a.signs != nullptr;
+    const u32x4 smask = sign_masks(a.signs, ck);
+    // The unnormalised butterfly, then one multiply by 1/sqrt(d) at the end:
+    // rounding is monotone and odd, so max_i |fl(x_i / sqrt(d))| equals
+    // fl(max_i |x_i| / sqrt(d)), the largest transformed magnitude.
     float m[3] = {0.0f, 0.0f, 0.0f};
-    // every pass's loads are issued before any is used
-    u32x4 rq[NP], rk[NP], rv[NP];
+    for (int blk = 0; blk < kAmaxBlocks; ++blk) {
+        const int r0 = (blockIdx.y * kAmaxBlocks + blk) * kQuantRows;
+        // every pass's loads are issued before any is used
+        u32x4 rq[NP], rk[NP], rv[NP];
 #pragma unroll
-    for (int pass = 0; pass < NP; ++pass) {
-        const int row = r0 + pass * RPI + tid / CH;
-        rq[pass] = load_once(static_cast<const T *>(a.q) + ((size_t)bh * a.Nq + row) * D + 8 * lc, row < a.Nq);
-        rk[pass] = load_once(static_cast<const T *>(a.k) + ((size_t)bh * a.Nk + row) * D + 8 * lc, row < a.Nk);
-        rv[pass] = load_once(static_cast<const T *>(a.v) + ((size_t)bh * a.Nk + row) * D + 8 * lc, row < a.Nk);
+        for (int pass = 0; pass < NP; ++pass) {
+            const int row = r0 + pass * RPI + tid / CH;
+            rq[pass] = load_once(static_cast<const T *>(a.q) + ((size_t)bh * a.Nq + row) * D + 8 * ck, row < a.Nq);
+            rk[pass] = load_once(static_cast<const T *>(a.k) + ((size_t)bh * a.Nk + row) * D + 8 * ck, row < a.Nk);
+            rv[pass] = load_once(static_cast<const T *>(a.v) + ((size_t)bh * a.Nk + row) * D + 8 * ck, row < a.Nk);
+        }
+#pragma unroll
+        for (int pass = 0; pass < NP; ++pass) {
+            const int row = r0 + pass * RPI + tid / CH;
+            float x[8];
+            if (row < a.Nq) {  // CH lanes share the row: the group is uniform, the exchanges stay inside it
+                unpack8<T>(rq[pass] ^ smask, x);
+                transform_row<D, false>(x, has_signs, ck);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) m[0] = __builtin_fmaxf(m[0], __builtin_fabsf(x[e]));
+            }
+            if (row < a.Nk) {
+                unpack8<T>(rk[pass] ^ smask, x);
+                transform_row<D, false>(x, has_signs, ck);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) m[1] = __builtin_fmaxf(m[1], __builtin_fabsf(x[e]));
+                unpack8<T>(rv[pass], x);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) m[2] = __builtin_fmaxf(m[2], __builtin_fabsf(x[e]));
+            }
+        }
     }
-#pragma unroll
-    for (int pass = 0; pass < NP; ++pass) {
-        const int row = r0 + pass * RPI + tid / CH;
-        float x[8];
-        if (row < a.Nq) {  // CH lanes share the row: the group is uniform, the exchanges stay inside it
-            unpack8<T>(rq[pass], x);
-            transform_row<D>(x, a.signs, lc);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) m[0] = __builtin_fmaxf(m[0], __builtin_fabsf(x[e]));
-        }
-        if (row < a.Nk) {
-            unpack8<T>(rk[pass], x);
-            transform_row<D>(x, a.signs, lc);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) m[1] = __builtin_fmaxf(m[1], __builtin_fabsf(x[e]));
-            unpack8<T>(rv[pass], x);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) m[2] = __builtin_fmaxf(m[2], __builtin_fabsf(x[e]));
-        }
+    if (has_signs) {
+        const float norm = (float)(1.0 / __builtin_sqrt((double)D));
+        m[0] *= norm;
+        m[1] *= norm;
     }
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
 #pragma unroll
         for (int msk = 32; msk > 0; msk >>= 1) m[t] = __builtin_fmaxf(m[t], __shfl_xor(m[t], msk));
+        if ((tid & 63) == 0) wmax[tid >> 6][t] = m[t];
+    }
+    __syncthreads();
+    if (tid < 3) {
+        float r = wmax[0][tid];
+#pragma unroll
+        for (int w = 1; w < kQuantThreads / 64; ++w) r = __builtin_fmaxf(r, wmax[w][tid]);
         // non-negative floats order like their bit patterns
-        if ((tid & 63) == 0) atomicMax(&a.pack.amax[t * a.BH + bh], __float_as_uint(m[t]));
+        atomicMax(&a.pack.amax[tid * a.BH + bh], __float_as_uint(r));
     }
 }
 
@@ -237,7 +274,9 @@ __global__ __launch_bounds__(kQuantThreads) void fp8_quantize_kernel(QuantArgs a
     const int bh = blockIdx.x;
     const int r0 = blockIdx.y * kQuantRows;
     const int tid = threadIdx.x;
-    const int lc = tid % CH;
+    const int ck = chunk_of_lane(tid % CH);
+    const bool has_signs = a.signs != nullptr;
+    const u32x4 smask = sign_masks(a.signs, ck);
     const float iq = inv_scale(a.pack.amax[bh]);
     const float ik = inv_scale(a.pack.amax[a.BH + bh]);
     const float iv = inv_scale(a.pack.amax[2 * a.BH + bh]);
@@ -251,9 +290,9 @@ __global__ __launch_bounds__(kQuantThreads) void fp8_quantize_kernel(QuantArgs a
 #pragma unroll
     for (int pass = 0; pass < NP; ++pass) {
         const int row = r0 + pass * RPI + tid / CH;
-        rq[pass] = load_once(static_cast<const T *>(a.q) + ((size_t)bh * a.Nq + row) * D + 8 * lc, row < a.Nq);
-        rk[pass] = load_once(static_cast<const T *>(a.k) + ((size_t)bh * a.Nk + row) * D + 8 * lc, row < a.Nk);
-        rv[pass] = load_once(static_cast<const T *>(a.v) + ((size_t)bh * a.Nk + row) * D + 8 * lc, row < a.Nk);
+        rq[pass] = load_once(static_cast<const T *>(a.q) + ((size_t)bh * a.Nq + row) * D + 8 * ck, row < a.Nq);
+        rk[pass] = load_once(static_cast<const T *>(a.k) + ((size_t)bh * a.Nk + row) * D + 8 * ck, row < a.Nk);
+        rv[pass] = load_once(static_cast<const T *>(a.v) + ((size_t)bh * a.Nk + row) * D + 8 * ck, row < a.Nk);
     }
 #pragma unroll
     for (int pass = 0; pass < NP; ++pass) {
@@ -261,26 +300,26 @@ __global__ __launch_bounds__(kQuantThreads) void fp8_quantize_kernel(QuantArgs a
         const int row = r0 + rl;
         float x[8];
         if (row < a.Nq) {
-            unpack8<T>(rq[pass], x);
-            transform_row<D>(x, a.signs, lc);
+            unpack8<T>(rq[pass] ^ smask, x);
+            transform_row<D, true>(x, has_signs, ck);
             u32x2 c;
             c[0] = to_e4m3x4(clamp448(x[0] * iq), clamp448(x[1] * iq), clamp448(x[2] * iq), clamp448(x[3] * iq));
             c[1] = to_e4m3x4(clamp448(x[4] * iq), clamp448(x[5] * iq), clamp448(x[6] * iq), clamp448(x[7] * iq));
-            *reinterpret_cast<u32x2 *>(a.pack.q8 + ((size_t)bh * a.Nq + row) * D + 8 * lc) = c;
+            *reinterpret_cast<u32x2 *>(a.pack.q8 + ((size_t)bh * a.Nq + row) * D + 8 * ck) = c;
         }
         if (row < a.Nkp) {  // key rows past Nk (padding up to the group) are zero codes
             u32x2 c = {0u, 0u}, cv = {0u, 0u};
             if (row < a.Nk) {
-                unpack8<T>(rk[pass], x);
-                transform_row<D>(x, a.signs, lc);
+                unpack8<T>(rk[pass] ^ smask, x);
+                transform_row<D, true>(x, has_signs, ck);
                 c[0] = to_e4m3x4(clamp448(x[0] * ik), clamp448(x[1] * ik), clamp448(x[2] * ik), clamp448(x[3] * ik));
                 c[1] = to_e4m3x4(clamp448(x[4] * ik), clamp448(x[5] * ik), clamp448(x[6] * ik), clamp448(x[7] * ik));
                 unpack8<T>(rv[pass], x);
                 cv[0] = to_e4m3x4(clamp448(x[0] * iv), clamp448(x[1] * iv), clamp448(x[2] * iv), clamp448(x[3] * iv));
                 cv[1] = to_e4m3x4(clamp448(x[4] * iv), clamp448(x[5] * iv), clamp448(x[6] * iv), clamp448(x[7] * iv));
             }
-            *reinterpret_cast<u32x2 *>(a.pack.k8 + ((size_t)bh * a.Nkp + row) * D + 8 * lc) = c;
-            *reinterpret_cast<u32x2 *>(&vtile[rl][8 * lc]) = cv;
+            *reinterpret_cast<u32x2 *>(a.pack.k8 + ((size_t)bh * a.Nkp + row) * D + 8 * ck) = c;
+            *reinterpret_cast<u32x2 *>(&vtile[rl][8 * ck]) = cv;
         }
     }
     __syncthreads();
@@ -612,7 +651,9 @@ hipError_t quantize_typed(const QuantArgs &a, hipStream_t stream) {
     if (err != hipSuccess) return err;
     const int rows = a.Nq > a.Nkp ? a.Nq : a.Nkp;
     const dim3 grid((unsigned)a.BH, (unsigned)((rows + kQuantRows - 1) / kQuantRows));
-    hipLaunchKernelGGL((fp8_amax_kernel<T, D>), grid, dim3(kQuantThreads), 0, stream, a);
+    const int amax_rows = kQuantRows * kAmaxBlocks;
+    const dim3 agrid((unsigned)a.BH, (unsigned)((rows + amax_rows - 1) / amax_rows));
+    hipLaunchKernelGGL((fp8_amax_kernel<T, D>), agrid, dim3(kQuantThreads), 0, stream, a);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((fp8_quantize_kernel<T, D>), grid, dim3(kQuantThreads), 0, stream, a);
