@@ -28,7 +28,8 @@
  * Ownership.  Every pointer is device memory owned by the caller; the
  * library never frees or retains it.  out and lse must not overlap q, k or
  * v.  The library owns only the split-KV workspace cache of ``fa_fwd``
- * (released by ``fa_release_workspace``).
+ * (decode, and prefill grids too small for the GPU; released by
+ * ``fa_release_workspace``).
  *
  * Asynchrony.  Every entry point enqueues its kernels on ``stream`` and
  * returns; results are valid once the stream has completed that work.  A
@@ -80,7 +81,17 @@ typedef enum fa_status {
  * path ("6. FlashAttention 分块逻辑", section 11: K/V split into chunks that
  * are processed independently, then merged by logsumexp weights) with
  * fa_default_num_splits(Nk) chunks and a library-owned workspace kept per
- * (device, stream); any other shape runs the tiled prefill kernel.
+ * (device, stream); any other shape runs the tiled prefill kernel.  A
+ * 16-bit prefill whose grid of (batch*head, Q block) workgroups is too small
+ * to give every CU two of them (fewer than 512), and whose Q blocks read
+ * enough K/V tiles (the causal mask counted: 32 for grids of at most 128
+ * workgroups, 256 above), has the key range of each Q block cut into
+ * min(ceil(512 / grid), tiles / 8, 64) chunks of whole K/V tiles as well
+ * (fewer where whole-tile chunks need fewer), one workgroup each, and
+ * the chunks merged by the same logsumexp combine, through the same
+ * library-owned workspace (B*H*Nq*chunks*(d + 1) float32).  The environment
+ * variable FA_PREFILL_SPLIT overrides the choice: 0 or 1 never splits, n >= 2
+ * asks for n chunks (capped at the tile count).
  */
 int fa_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
            int B, int H, int Nq, int Nk, int d, float scale, int causal,

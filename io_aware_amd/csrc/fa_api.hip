@@ -89,7 +89,8 @@ int prefill_shape(int d) {
     return d >= 128 ? fa::kShapeW4Q32B32 : fa::kShapeW4Q32;
 }
 
-// Library-owned decode workspaces, one per (device, stream).
+// Library-owned split workspaces (decode, and split prefill), one per
+// (device, stream).
 struct Workspace {
     void *ptr = nullptr;
     size_t bytes = 0;
@@ -152,9 +153,18 @@ int fa_fwd(const void *q, const void *k, const void *v, void *out, float *lse, i
     if (dtype == FA_F32)
         return hip_status(fa::launch_prefill_f32(d, causal == 1, q, k, v, out, lse, B * H, Nq, Nk, sl, stream),
                           "fp32 prefill launch");
-    return hip_status(
-        fa::launch_prefill(dtype, d, causal == 1, prefill_shape(d), q, k, v, out, lse, B * H, Nq, Nk, sl, stream),
-        "prefill launch");
+    const int shape = prefill_shape(d);
+    const int S = fa::prefill_split_count(d, causal == 1, shape, B * H, Nq, Nk);
+    if (S > 1) {  // a grid too small for the GPU: split the key range, then combine
+        void *ws = nullptr;
+        st = get_workspace(workspace_bytes(B, H, Nq, d, S), stream, &ws);
+        if (st != FA_OK) return st;
+        return hip_status(fa::launch_prefill_split(dtype, d, causal == 1, shape, q, k, v, out, lse, B * H, Nq, Nk,
+                                                   sl, S, ws, stream),
+                          "split prefill launch");
+    }
+    return hip_status(fa::launch_prefill(dtype, d, causal == 1, shape, q, k, v, out, lse, B * H, Nq, Nk, sl, stream),
+                      "prefill launch");
 }
 
 size_t fa_splitkv_workspace_bytes(int B, int H, int Nq, int d, int num_splits) {

@@ -314,6 +314,32 @@ hipError_t launch_any(int dtype, int d, const SplitArgs &a, void *out, float *ls
 
 }  // namespace
 
+hipError_t launch_combine(int dtype, int d, const float *ws_o, const float *ws_lse, void *out, float *lse,
+                          int rows, int S, hipStream_t stream) {
+    if (S < 1 || S > kMaxSplits || rows < 1) return hipErrorInvalidConfiguration;
+    CombineArgs b;
+    b.ws_o = ws_o;
+    b.ws_lse = ws_lse;
+    b.out = out;
+    b.lse = lse;
+    b.rows = rows;
+    b.S = S;
+    const dim3 grid((unsigned)((rows + 3) / 4));
+#define FA_CASE(DD)                                                                                      \
+    case DD:                                                                                             \
+        if (dtype == 2) hipLaunchKernelGGL((splitkv_combine_kernel<__bf16, DD>), grid, dim3(256), 0, stream, b); \
+        else hipLaunchKernelGGL((splitkv_combine_kernel<_Float16, DD>), grid, dim3(256), 0, stream, b);          \
+        return hipGetLastError();
+    if (dtype != 1 && dtype != 2) return hipErrorInvalidValue;
+    switch (d) {
+        FA_CASE(32)
+        FA_CASE(64)
+        FA_CASE(128)
+        default: return hipErrorInvalidValue;
+    }
+#undef FA_CASE
+}
+
 hipError_t launch_splitkv(int dtype, int d, const void *q, const void *k, const void *v, void *out, float *lse,
                           int BH, int Nk, float scale_log2, int num_splits, void *workspace, hipStream_t stream) {
     SplitArgs a = {};

@@ -40,6 +40,23 @@ hipError_t launch_prefill_varlen(int dtype, int d, bool causal, int shape, const
                                  int H, int total_q, int total_k, float scale_log2, void *workspace,
                                  hipStream_t stream);
 
+// Split prefill for grids too small to fill the GPU: the key range of every
+// (batch*head, Q block) is cut into S chunks of whole K/V tiles, one
+// workgroup each; every chunk writes its normalised partial output and its
+// logsumexp (the split-KV stage-one layout: o~ [rows, S, d] float32 then
+// lse_c [rows, S], rows = BH * Nq) into workspace, and the split-KV combine
+// merges them into out and lse.  prefill_split_count chooses S (1: no split;
+// FA_PREFILL_SPLIT = 0 disables, a number n >= 2 asks for n chunks).
+int prefill_split_count(int d, bool causal, int shape, int BH, int Nq, int Nk);
+hipError_t launch_prefill_split(int dtype, int d, bool causal, int shape, const void *q, const void *k,
+                                const void *v, void *out, float *lse, int BH, int Nq, int Nk, float scale_log2,
+                                int S, void *workspace, hipStream_t stream);
+
+// The split-KV combine alone: out [rows, d] (dtype) and lse [rows] from the
+// chunk partials o~ [rows, S, d] and lse_c [rows, S].
+hipError_t launch_combine(int dtype, int d, const float *ws_o, const float *ws_lse, void *out, float *lse,
+                          int rows, int S, hipStream_t stream);
+
 // float32 tiled forward (vector ALU), Br = Bc = 64.
 hipError_t launch_prefill_f32(int d, bool causal, const void *q, const void *k,
                               const void *v, void *out, float *lse, int BH,

@@ -46,6 +46,7 @@
 //    causal blocks first (fa_layout.h).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "fa_device.h"
 #include "fa_internal.h"
@@ -73,16 +74,30 @@ struct PrefillArgs {
     int H;
     int total_q;
     int total_k;
+    // split prefill: the key range of a Q block is cut into S chunks of
+    // `chunk` keys (a multiple of the tile); partials go to ws_o / ws_lse
+    float *ws_o;    // [BH * Nq, S, D]
+    float *ws_lse;  // [BH * Nq, S]
+    int S;
+    int chunk;
 };
+
+// How a launch maps workgroups to work: dense (batch*head, Q block),
+// packed variable-length tiles, or dense with the key range split.
+constexpr int kModeDense = 0;
+constexpr int kModeVarlen = 1;
+constexpr int kModeSplit = 2;
 
 // Bound on a lane's per-tile sum of P between rescales; it keeps every
 // P <= 2^8 (see the online-softmax step of prefill_kernel).
 constexpr float kHeldSumBound = 256.0f;
 constexpr float kLn2 = 0.693147180559945309417f;
 
-template <typename T, int D, bool CAUSAL, int NW, int QW, int BC, int OCC, bool VARLEN>
+template <typename T, int D, bool CAUSAL, int NW, int QW, int BC, int OCC, int MODE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC)))
 void prefill_kernel(PrefillArgs a) {
+    constexpr bool VARLEN = MODE == kModeVarlen;
+    constexpr bool SPLIT = MODE == kModeSplit;
     using M = Mfma<T>;
     using x8 = typename M::x8;
     using x4 = typename M::x4;
@@ -112,9 +127,10 @@ void prefill_kernel(PrefillArgs a) {
     const int g = lane >> 5;
 
     // Work item: (batch*head, Q block) of a dense launch, or (head, tile of
-    // the schedule) of a packed variable-length launch.  RS is the element
-    // stride between consecutive rows of one head.
-    int qblk, Nq, Nk, RS;
+    // the schedule) of a packed variable-length launch, or (batch*head, Q
+    // block, key chunk) of a split launch.  RS is the element stride between
+    // consecutive rows of one head.
+    int qblk, Nq, Nk, RS, bh = 0, chunk_idx = 0;
     const T *qp, *kp, *vp;
     T *op;
     float *lsep;
@@ -136,8 +152,12 @@ void prefill_kernel(PrefillArgs a) {
         op = static_cast<T *>(a.out) + ((size_t)qs * a.H + h) * D;
         lsep = a.lse ? a.lse + (size_t)h * a.total_q + qs : nullptr;
     } else {
-        int bh;
-        layout::map_workgroup(blockIdx.x, a.BH, a.Tr, CAUSAL, bh, qblk);
+        int wg = blockIdx.x;
+        if constexpr (SPLIT) {  // the chunks of one Q block are neighbours
+            chunk_idx = wg % a.S;
+            wg /= a.S;
+        }
+        layout::map_workgroup(wg, a.BH, a.Tr, CAUSAL, bh, qblk);
         Nq = a.Nq;
         Nk = a.Nk;
         RS = D;
@@ -221,7 +241,10 @@ void prefill_kernel(PrefillArgs a) {
     }
 
     const int kv_end = CAUSAL ? min(Nk, q0 + BR) : Nk;
-    const int nt = (kv_end + BC - 1) / BC;
+    // keys [kbeg, kend) of this workgroup: all visible ones, or one chunk
+    const int kbeg = SPLIT ? min(kv_end, chunk_idx * a.chunk) : 0;
+    const int kend = SPLIT ? min(kv_end, kbeg + a.chunk) : kv_end;
+    const int nt = (kend - kbeg + BC - 1) / BC;
 
     auto compute_tile = [&](auto stage_tag, int k0) {
         constexpr int S = decltype(stage_tag)::value;
@@ -332,7 +355,7 @@ void prefill_kernel(PrefillArgs a) {
 
     auto step = [&](auto stage_tag, int jt) {
         constexpr int S = decltype(stage_tag)::value;
-        const int k0 = jt * BC;
+        const int k0 = kbeg + jt * BC;
         if (jt + 1 < nt) issue_tile(k0 + BC, S ^ 1);
         // wave-uniform: the wave has live queries that see some key of this block
         const bool active = (q0w < Nq) && (!CAUSAL || k0 <= q0w + QW - 1);
@@ -341,8 +364,8 @@ void prefill_kernel(PrefillArgs a) {
         __syncthreads();                                    // ... and every thread's; stage S is free
     };
 
-    if (nt > 0) {  // workgroup-uniform; a sequence without keys has no tile
-        issue_tile(0, 0);
+    if (nt > 0) {  // workgroup-uniform; a sequence (or chunk) without keys has no tile
+        issue_tile(kbeg, 0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
@@ -352,25 +375,41 @@ void prefill_kernel(PrefillArgs a) {
     }
 
     // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2 --------------------
+    // (split launch: this chunk's normalised partial o~ = acc / l and its
+    // logsumexp, -inf with o~ = 0 where the chunk holds no visible key)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const float l = xor32_sum(l_part[qb]);
         const int row = q0w + 32 * qb + l32;
         if (row < Nq) {
             const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
+            const float lse_row = (l > 0.0f) ? (m_held[qb] + __builtin_amdgcn_logf(l)) * kLn2 : -__builtin_inff();
+            if constexpr (SPLIT) {
+                const size_t slot = ((size_t)bh * Nq + row) * a.S + chunk_idx;
+                float *wo = a.ws_o + slot * D;
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
+                for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int rg = 0; rg < 4; ++rg) {
-                    f32x4 t;
+                    for (int rg = 0; rg < 4; ++rg) {
+                        f32x4 t;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) t[e] = oacc[qb][db][4 * rg + e] * inv;
-                    const x4 o = __builtin_convertvector(t, x4);
-                    *reinterpret_cast<x4 *>(op + (size_t)row * RS + 32 * db + 8 * rg + 4 * g) = o;
-                }
-            if (g == 0 && lsep != nullptr)
-                lsep[row] =
-                    (l > 0.0f) ? (m_held[qb] + __builtin_amdgcn_logf(l)) * kLn2 : -__builtin_inff();
+                        for (int e = 0; e < 4; ++e) t[e] = oacc[qb][db][4 * rg + e] * inv;
+                        *reinterpret_cast<f32x4 *>(wo + 32 * db + 8 * rg + 4 * g) = t;
+                    }
+                if (g == 0) a.ws_lse[slot] = lse_row;
+            } else {
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int rg = 0; rg < 4; ++rg) {
+                        f32x4 t;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) t[e] = oacc[qb][db][4 * rg + e] * inv;
+                        const x4 o = __builtin_convertvector(t, x4);
+                        *reinterpret_cast<x4 *>(op + (size_t)row * RS + 32 * db + 8 * rg + 4 * g) = o;
+                    }
+                if (g == 0 && lsep != nullptr) lsep[row] = lse_row;
+            }
         }
     }
 }
@@ -495,7 +534,14 @@ hipError_t launch_one(const PrefillArgs &base, bool varlen, int S, hipStream_t s
         a.Tr = (a.Nq + BR - 1) / BR;
         const long long nwg = (long long)a.BH * a.Tr;
         if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((prefill_kernel<T, D, CAUSAL, NW, QW, BC, OCC, false>), dim3((unsigned)nwg),
+        if (a.S > 1) {
+            const long long nwg_split = nwg * a.S;
+            if (nwg_split > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+            hipLaunchKernelGGL((prefill_kernel<T, D, CAUSAL, NW, QW, BC, OCC, kModeSplit>), dim3((unsigned)nwg_split),
+                               dim3(NW * 64), 0, stream, a);
+            return hipGetLastError();
+        }
+        hipLaunchKernelGGL((prefill_kernel<T, D, CAUSAL, NW, QW, BC, OCC, kModeDense>), dim3((unsigned)nwg),
                            dim3(NW * 64), 0, stream, a);
         return hipGetLastError();
     }
@@ -507,8 +553,8 @@ hipError_t launch_one(const PrefillArgs &base, bool varlen, int S, hipStream_t s
                        a.cu_k, S, a.total_q, a.total_k, (int)tiles, sched);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((prefill_kernel<T, D, CAUSAL, NW, QW, BC, OCC, true>), dim3((unsigned)nwg), dim3(NW * 64), 0,
-                       stream, a);
+    hipLaunchKernelGGL((prefill_kernel<T, D, CAUSAL, NW, QW, BC, OCC, kModeVarlen>), dim3((unsigned)nwg),
+                       dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -558,6 +604,76 @@ int prefill_block_rows(int shape) {
         case kShapeW4Q32B32: return 128;
         default: return 0;
     }
+}
+
+// Keys per K/V tile of a shape at head dim d (shape 3 falls back to shape 0
+// below d = 64).
+static int prefill_block_cols(int shape, int d) { return (shape == kShapeW4Q32B32 && d >= 64) ? 32 : 64; }
+
+// K/V tiles in the longest key range a Q block reads: all Nk keys, or under
+// the causal mask (query i sees keys 0..i) at most the rows of the last Q
+// block.  Split chunks cover this range only.
+static int split_key_tiles(int shape, int d, bool causal, int Nq, int Nk) {
+    const int br = prefill_block_rows(shape), bc = prefill_block_cols(shape, d);
+    const long long rows = (long long)(Nq + br - 1) / br * br;
+    const int kext = causal && rows < Nk ? (int)rows : Nk;
+    return (kext + bc - 1) / bc;
+}
+
+int prefill_split_count(int d, bool causal, int shape, int BH, int Nq, int Nk) {
+    const int br = prefill_block_rows(shape);
+    if (br <= 0 || BH < 1 || Nq < 1 || Nk < 1) return 1;
+    const long long grid = (long long)BH * ((Nq + br - 1) / br);
+    const int key_tiles = split_key_tiles(shape, d, causal, Nq, Nk);
+    int S;
+    const char *env = getenv("FA_PREFILL_SPLIT");
+    if (env != nullptr && env[0] != '\0') {
+        S = atoi(env);  // 0 or 1: never split; n: n chunks (at most one tile each)
+        if (S < 2) return 1;
+        S = S < key_tiles ? S : key_tiles;
+    } else {
+        // Split only when the grid cannot give every CU two workgroups and
+        // the key loop is long enough to pay for the fixed cost of a chunk
+        // and of the combine launch (about 6 us together): 32 tiles while
+        // at most half the CUs have a workgroup, 256 tiles beyond that,
+        // where the chunks must share CUs.  Keep at least 8 tiles per chunk.
+        constexpr long long kTargetGrid = 512;
+        const int min_tiles = grid <= 128 ? 32 : 256;
+        if (grid >= kTargetGrid || key_tiles < min_tiles) return 1;
+        S = (int)((kTargetGrid + grid - 1) / grid);
+        const int by_len = key_tiles / 8;
+        S = S < by_len ? S : by_len;
+        S = S < 64 ? S : 64;
+    }
+    if (S < 2) return 1;
+    // whole tiles per chunk; drop chunks that would start past the keys
+    const int chunk_tiles = (key_tiles + S - 1) / S;
+    return (key_tiles + chunk_tiles - 1) / chunk_tiles;
+}
+
+hipError_t launch_prefill_split(int dtype, int d, bool causal, int shape, const void *q, const void *k,
+                                const void *v, void *out, float *lse, int BH, int Nq, int Nk, float scale_log2,
+                                int S, void *workspace, hipStream_t stream) {
+    const int bc = prefill_block_cols(shape, d);
+    const int key_tiles = split_key_tiles(shape, d, causal, Nq, Nk);
+    if (S < 2 || S > key_tiles) return hipErrorInvalidValue;
+    PrefillArgs a = {};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.lse = lse;
+    a.BH = BH;
+    a.Nq = Nq;
+    a.Nk = Nk;
+    a.scale_log2 = scale_log2;
+    a.S = S;
+    a.chunk = (key_tiles + S - 1) / S * bc;
+    a.ws_o = static_cast<float *>(workspace);
+    a.ws_lse = a.ws_o + (size_t)BH * Nq * S * d;
+    hipError_t err = launch_any(dtype, d, causal, shape, a, false, 0, stream);
+    if (err != hipSuccess) return err;
+    return launch_combine(dtype, d, a.ws_o, a.ws_lse, out, lse, BH * Nq, S, stream);
 }
 
 long long varlen_max_tiles(int S, int total_q, int block_rows) {

@@ -104,18 +104,66 @@ SHAPES = [(1, 2, 300, 517), (2, 1, 517, 300), (1, 1, 129, 64), (1, 3, 64, 1), (1
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_ragged_shapes(fa, dtype, d, causal):
+@pytest.mark.parametrize("split", ["never", "auto"])
+def test_ragged_shapes(fa, dtype, d, causal, split, monkeypatch):
+    """Small grids: "auto" lets fa_fwd split the key range (these grids are
+    below the split threshold), "never" keeps one workgroup per Q block."""
+    if split == "never":
+        monkeypatch.setenv("FA_PREFILL_SPLIT", "0")
+    else:
+        monkeypatch.delenv("FA_PREFILL_SPLIT", raising=False)
     for i, (B, H, Nq, Nk) in enumerate(SHAPES):
-        run_full(fa, B, H, Nq, Nk, d, dtype, causal, seed=100 + i + 10 * d)
+        run_full(fa, B, H, Nq, Nk, d, dtype, causal, seed=100 + i + 10 * d,
+                 label="B%d H%d Nq%d Nk%d d%d %s causal=%d split=%s" % (B, H, Nq, Nk, d, dtype, causal, split))
 
 
 @pytest.mark.parametrize("shape_id", [0, 1, 2, 3])
-def test_every_prefill_tile_shape(fa, shape_id, monkeypatch):
+@pytest.mark.parametrize("split", ["0", "3"])
+def test_every_prefill_tile_shape(fa, shape_id, split, monkeypatch):
     monkeypatch.setenv("FA_PREFILL_SHAPE", str(shape_id))
+    monkeypatch.setenv("FA_PREFILL_SPLIT", split)
     for d in (64, 128):
         for causal in (False, True):
             run_full(fa, 1, 2, 700, 700, d, "bf16", causal, seed=7 + d, q_sigma=4.0,
-                     label="shape %d d%d causal=%d" % (shape_id, d, causal))
+                     label="shape %d d%d causal=%d split=%s" % (shape_id, d, causal, split))
+
+
+@pytest.mark.parametrize("split", ["2", "5", "64"])
+def test_split_prefill_chunk_counts(fa, split, monkeypatch):
+    """The split path at forced chunk counts (64 is capped at one tile per
+    chunk): ragged key counts, masks, key counts below and above the query
+    count, large score magnitudes."""
+    monkeypatch.setenv("FA_PREFILL_SPLIT", split)
+    cases = [(1, 2, 1000, 1000, 64, "f16", True), (2, 1, 333, 1500, 128, "bf16", False),
+             (1, 1, 1500, 333, 128, "bf16", True), (1, 3, 77, 4097, 64, "bf16", True),
+             (1, 1, 640, 640, 32, "f16", False)]
+    for i, (B, H, Nq, Nk, d, dtype, causal) in enumerate(cases):
+        run_full(fa, B, H, Nq, Nk, d, dtype, causal, seed=700 + i, q_sigma=4.0,
+                 label="split=%s B%d H%d Nq%d Nk%d d%d %s causal=%d" % (split, B, H, Nq, Nk, d, dtype, causal))
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,d,dtype,causal,chunks", [
+    (1, 2, 300, 5000, 64, "bf16", False, 9),     # grid 6, 79 tiles of 64 keys: 9 chunks of 9 tiles
+    (1, 1, 2500, 6000, 128, "bf16", True, 10),   # grid 20; the mask leaves 2560 keys = 80 tiles of 32
+    (1, 4, 500, 2100, 32, "f16", False, 4),      # grid 16, 33 tiles: 4 chunks of 9 tiles
+    (2, 4, 1000, 1000, 64, "f16", True, 1),      # 16 tiles per Q block: too short to split
+    (3, 48, 128, 2048, 32, "f16", False, 1),     # grid 144 with 32 tiles: chunks would share CUs
+])
+def test_split_prefill_automatic_choice(fa, B, H, Nq, Nk, d, dtype, causal, chunks, monkeypatch):
+    """Without FA_PREFILL_SPLIT, a grid under 512 workgroups whose Q blocks
+    read at least 32 K/V tiles (256 above 128 workgroups) is split into
+    min(ceil(512 / grid), tiles / 8, 64) chunks (then as many as whole-tile
+    chunks need): parity with the oracle, and bitwise the result of asking
+    for that chunk count."""
+    monkeypatch.delenv("FA_PREFILL_SPLIT", raising=False)
+    q, k, v, _, _ = run_full(fa, B, H, Nq, Nk, d, dtype, causal, seed=760 + d, q_sigma=4.0,
+                       label="auto split B%d H%d Nq%d Nk%d d%d %s causal=%d" % (B, H, Nq, Nk, d, dtype, causal))
+    qd, kd, vd = to_dev(q, k, v)
+    auto = fa.fa_fwd(qd, kd, vd, causal=causal)
+    monkeypatch.setenv("FA_PREFILL_SPLIT", str(chunks))
+    forced = fa.fa_fwd(qd, kd, vd, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(auto[0], forced[0]) and torch.equal(auto[1], forced[1])
 
 
 @pytest.mark.parametrize("shape_id", [0, 3])
