@@ -155,7 +155,8 @@ def cpu_baseline(w, q, k, v, target_s: float):
 
 
 def time_steps(step, steps, warmup, prewarm_s):
-    """(ms per step over the timed region, mean per-launch kernel ms)."""
+    """(ms per step over the timed region, mean per-step kernel ms from the
+    events, {median, min} of those per-step times)."""
     import torch
     dev = torch.device("cuda:0")
     t_end = time.perf_counter() + prewarm_s
@@ -176,8 +177,10 @@ def time_steps(step, steps, warmup, prewarm_s):
         e.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = [s.elapsed_time(e) for s, e in ev]
-    return wall * 1e3 / steps, sum(launch_ms) / len(launch_ms)
+    t = sorted(s.elapsed_time(e) for s, e in ev)
+    n = len(t)
+    spread = {"kernel_ms_median": t[n // 2] if n % 2 else 0.5 * (t[n // 2 - 1] + t[n // 2]), "kernel_ms_min": t[0]}
+    return wall * 1e3 / steps, sum(t) / n, spread
 
 
 def run_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s=0.3):
@@ -199,7 +202,7 @@ def run_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s=0.3):
     if w.fp8:
         signs = fa_inputs.make_signs(w.d, w.seed).to(dev)
         pack = fa.fa_quantize_fp8(qd, kd, vd, signs=signs)
-        qms, _ = time_steps(lambda: fa.fa_quantize_fp8(qd, kd, vd, signs=signs, pack=pack), 5, 1, 0.0)
+        qms, _, _ = time_steps(lambda: fa.fa_quantize_fp8(qd, kd, vd, signs=signs, pack=pack), 5, 1, 0.0)
         extra["quantize_ms"] = qms
 
         def step():
@@ -222,7 +225,7 @@ def run_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s=0.3):
         def step():
             fa.fa_fwd(qd, kd, vd, scale=w.scale, causal=w.causal, out=out, lse=lse)
 
-    ms_per_step, kernel_ms = time_steps(step, steps, warmup, prewarm_s)
+    ms_per_step, kernel_ms, spread = time_steps(step, steps, warmup, prewarm_s)
     flops = workload_flops(w)
     nbytes = workload_bytes(w)
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -239,7 +242,7 @@ def run_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s=0.3):
     rec = {
         "metric": "attention fwd TFLOP/s (and % of MI355X bf16 MFMA/HBM roofline) per config",
         "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
-        "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, "prewarm_s": prewarm_s,
+        "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, **spread, "prewarm_s": prewarm_s,
         "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "e4m3" if w.fp8 else w.dtype,
         "data": "synthetic (seeded randn, cast with RNE)",
@@ -291,7 +294,7 @@ def run_paged_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s):
     def step():
         fa.fa_fwd_paged_decode(qd, kcd, vcd, td, ld, w.num_splits, scale=w.scale, workspace=ws, out=out, lse=lse)
 
-    ms_per_step, kernel_ms = time_steps(step, steps, warmup, prewarm_s)
+    ms_per_step, kernel_ms, spread = time_steps(step, steps, warmup, prewarm_s)
     es = 2
     keys = int(lens.clamp(min=0).sum())
     flops = 4.0 * w.H * w.d * keys
@@ -303,7 +306,7 @@ def run_paged_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s):
     rec = {
         "metric": "attention fwd TFLOP/s (and % of MI355X bf16 MFMA/HBM roofline) per config",
         "value": flops / (ms_per_step * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
-        "warmup": warmup, "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, "prewarm_s": prewarm_s,
+        "warmup": warmup, "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, **spread, "prewarm_s": prewarm_s,
         "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded randn, shuffled block table)",
         "config": {"workload": name, "B": w.B, "H": w.H, "d": w.d, "block_size": w.block_size,
@@ -346,7 +349,7 @@ def run_varlen_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s):
     def step():
         fa.fa_fwd_varlen(qd, kd, vd, cqd, ckd, scale=w.scale, causal=w.causal, out=out, lse=lse, workspace=ws)
 
-    ms_per_step, kernel_ms = time_steps(step, steps, warmup, prewarm_s)
+    ms_per_step, kernel_ms, spread = time_steps(step, steps, warmup, prewarm_s)
     lq = (cq[1:] - cq[:-1]).tolist()
     lk = (ck[1:] - ck[:-1]).tolist()
     flops = 4.0 * w.d * w.H * varlen_pairs(w, lq, lk)
@@ -355,7 +358,7 @@ def run_varlen_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s):
     rec = {
         "metric": "attention fwd TFLOP/s (and % of MI355X bf16 MFMA/HBM roofline) per config",
         "value": flops / (ms_per_step * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
-        "warmup": warmup, "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, "prewarm_s": prewarm_s,
+        "warmup": warmup, "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, **spread, "prewarm_s": prewarm_s,
         "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded randn, seeded length mix)",
         "config": {"workload": name, "S": w.S, "H": w.H, "d": w.d, "causal": w.causal, "dtype": w.dtype,
