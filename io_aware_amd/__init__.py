@@ -88,23 +88,38 @@ def _check(status: int, where: str) -> None:
         raise FAError(status, where)
 
 
+_DTYPE_CODES = None
+_RAW_STREAM = None
+
+
 def _dtype_code(t) -> int:
-    import torch
-    codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
-    if t.dtype not in codes:
+    global _DTYPE_CODES
+    if _DTYPE_CODES is None:
+        import torch
+        _DTYPE_CODES = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+    code = _DTYPE_CODES.get(t.dtype)
+    if code is None:
         raise TypeError("unsupported dtype %s" % t.dtype)
-    return codes[t.dtype]
+    return code
 
 
 def _stream_handle(t, stream):
-    import torch
-    if stream is None:
-        stream = torch.cuda.current_stream(t.device)
-    return ctypes.c_void_p(stream.cuda_stream)
+    """The HIP stream handle (an int) to enqueue on: ``stream`` if given,
+    else the current stream of ``t``'s device.  The current stream is read
+    through torch's raw-handle accessor (a fraction of a microsecond) where
+    this torch has it, else through ``torch.cuda.current_stream``."""
+    global _RAW_STREAM
+    if stream is not None:
+        return stream.cuda_stream
+    if _RAW_STREAM is None:
+        import torch
+        _RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None) or \
+            (lambda index: torch.cuda.current_stream(index).cuda_stream)
+    return _RAW_STREAM(t.device.index)
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
 def _shapes(q, k, v):

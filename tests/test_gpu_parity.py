@@ -279,6 +279,43 @@ def test_guard_bands_untouched(fa, dtype, Nq, Nk, causal):
     compare(out, lse, ref_o, ref_l, dtype, "guard bands %s" % dtype)
 
 
+def _timed_on(stream, fn):
+    """Events on ``stream`` around ``fn()``: elapsed ms after the stream drains."""
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    r = fn()
+    e.record(stream)
+    stream.synchronize()
+    return r, s.elapsed_time(e)
+
+
+@pytest.mark.parametrize("Nq", [4096, 1])
+def test_side_stream(fa, Nq):
+    """The entry point enqueues on the caller's stream: the current stream
+    inside ``torch.cuda.stream(s)`` and the ``stream`` argument both give the
+    default stream's result bit for bit, and events recorded on the side
+    stream around the call span the kernels (a launch on another stream
+    would leave them about a kernel's length apart too soon).  Nq = 1 is the
+    decode path, with its per-stream library workspace."""
+    B, H, Nk, d = 2, 16, 4096, 128
+    q, k, v = fa_inputs.make_qkv_device(B, H, Nq, Nk, d, "bf16", seed=32, device=DEV)
+    causal = Nq > 1
+    main = torch.cuda.current_stream()
+    for _ in range(3):                                   # warm the clocks
+        fa.fa_fwd(q, k, v, causal=causal)
+    (ref_o, ref_l), t_main = _timed_on(main, lambda: fa.fa_fwd(q, k, v, causal=causal))
+    side = torch.cuda.Stream()                           # default priority
+    side.wait_stream(main)
+    with torch.cuda.stream(side):
+        (o1, l1), t1 = _timed_on(side, lambda: fa.fa_fwd(q, k, v, causal=causal))
+    (o2, l2), t2 = _timed_on(side, lambda: fa.fa_fwd(q, k, v, causal=causal, stream=side))
+    torch.cuda.synchronize()
+    for o, l in ((o1, l1), (o2, l2)):
+        assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+    assert t1 >= 0.5 * t_main and t2 >= 0.5 * t_main, (t_main, t1, t2)
+
+
 def test_lse_optional(fa):
     q, k, v = fa_inputs.make_qkv(1, 2, 100, 100, 64, "bf16", seed=26)
     qd, kd, vd = to_dev(q, k, v)
