@@ -254,10 +254,12 @@ __device__ __forceinline__ float inv_scale(uint32_t amax_bits) {
     return amax > 0.0f ? kE4M3Max / amax : 1.0f;
 }
 
-// four floats -> four E4M3 codes (round to nearest even), packed little-endian
+// four floats -> four E4M3 codes (round to nearest even), packed little-endian.
+// The first conversion writes bytes 0-1 of its "old" operand and keeps bytes
+// 2-3, which the second conversion overwrites: any word serves as "old", and
+// a's own bits avoid a register clear per word.
 __device__ __forceinline__ uint32_t to_e4m3x4(float a, float b, float c, float d) {
-    int w = 0;
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, w, false);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)__float_as_uint(a), false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
     return (uint32_t)w;
 }
