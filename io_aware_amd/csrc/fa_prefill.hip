@@ -258,15 +258,29 @@ void prefill_kernel(PrefillArgs a) {
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.0f;
+        // K fragments are read KPF steps ahead of the MFMA that takes them
+        constexpr int NK = KB * KS;
+        constexpr int KPF = NK < 4 ? NK : 4;
+        auto read_k = [&](int i) {
+            return __builtin_bit_cast(
+                x8, *reinterpret_cast<const u32x4 *>(smem + KOFF + (i / KS) * 32 * ROW + koff[i % KS]));
+        };
+        x8 kq[KPF];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+        for (int i = 0; i < KPF; ++i) kq[i] = read_k(i);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const x8 kf = __builtin_bit_cast(
-                    x8, *reinterpret_cast<const u32x4 *>(smem + KOFF + kb * 32 * ROW + koff[ks]));
+        for (int i = 0; i < NK; ++i) {
+            const x8 kf = kq[i % KPF];
+            if (i + KPF < NK) kq[i % KPF] = read_k(i + KPF);
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) s[qb][kb] = M::run(kf, qf[qb][ks], s[qb][kb]);
-            }
+            for (int qb = 0; qb < QB; ++qb) s[qb][i / KS] = M::run(kf, qf[qb][i % KS], s[qb][i / KS]);
+        }
+        // keep that order: KPF reads, then (QB MFMAs, one read) per step
+        __builtin_amdgcn_sched_group_barrier(0x100, KPF, 0);
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+            if (i + KPF < NK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
 
         // ---- mask: ragged key tail and the causal diagonal ------------------
