@@ -259,8 +259,10 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.0f;
         // K fragments are read KPF steps ahead of the MFMA that takes them
+        // (with 64 queries per wave each fragment feeds two MFMAs, which
+        // hides the read by itself: the compiler schedules those shapes)
         constexpr int NK = KB * KS;
-        constexpr int KPF = NK < 4 ? NK : 4;
+        constexpr int KPF = QB > 1 ? 1 : (NK < 4 ? NK : 4);
         auto read_k = [&](int i) {
             return __builtin_bit_cast(
                 x8, *reinterpret_cast<const u32x4 *>(smem + KOFF + (i / KS) * 32 * ROW + koff[i % KS]));
@@ -275,12 +277,14 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) s[qb][i / KS] = M::run(kf, qf[qb][i % KS], s[qb][i / KS]);
         }
-        // keep that order: KPF reads, then (QB MFMAs, one read) per step
-        __builtin_amdgcn_sched_group_barrier(0x100, KPF, 0);
+        // keep that order: KPF reads, then (one MFMA, one read) per step
+        if constexpr (QB == 1) {
+            __builtin_amdgcn_sched_group_barrier(0x100, KPF, 0);
 #pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
-            if (i + KPF < NK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            for (int i = 0; i < NK; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (i + KPF < NK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
         }
 
         // ---- mask: ragged key tail and the causal diagonal ------------------
@@ -353,16 +357,33 @@ void prefill_kernel(PrefillArgs a) {
         }
 
         // ---- O^T += V^T P^T -------------------------------------------------
+        // step i = (k-step i / DB, d block i % DB); its V^T fragment (two
+        // transposing reads) is read VPF steps ahead of its MFMA (at 32
+        // queries per wave, as for K)
+        constexpr int NV = KS2 * DB;
+        constexpr int VPF = QB > 1 ? 1 : (NV < 3 ? NV : 3);
+        auto read_v = [&](int i) {
+            const char *base = smem + VOFF + voff[i % DB] + 16 * (i / DB) * ROW;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4 *)(base));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4 *)(base + 8 * ROW));
+            return __builtin_bit_cast(x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        x8 vq[VPF];
 #pragma unroll
-        for (int ks2 = 0; ks2 < KS2; ++ks2) {
+        for (int i = 0; i < VPF; ++i) vq[i] = read_v(i);
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const char *base = smem + VOFF + voff[db] + 16 * ks2 * ROW;
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4 *)(base));
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4 *)(base + 8 * ROW));
-                const x8 vf = __builtin_bit_cast(x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        for (int i = 0; i < NV; ++i) {
+            const x8 vf = vq[i % VPF];
+            if (i + VPF < NV) vq[i % VPF] = read_v(i + VPF);
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = M::run(vf, pf[qb][ks2], oacc[qb][db]);
+            for (int qb = 0; qb < QB; ++qb) oacc[qb][i % DB] = M::run(vf, pf[qb][i / DB], oacc[qb][i % DB]);
+        }
+        if constexpr (QB == 1) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * VPF, 0);
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (i + VPF < NV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
         }
     };
