@@ -208,17 +208,44 @@ void bwd_dq_kernel(BwdArgs a) {
                 s[kb][r] = 0.0f;
                 dp[kb][r] = 0.0f;
             }
+        // step i = (block i / KS, k-step i % KS): at d = 128 its K and V
+        // fragments are read PF steps ahead of its two MFMAs (order pinned
+        // below; below d = 128 the registers this takes would cost a wave per
+        // SIMD, and the compiler schedules)
+        constexpr int NK = KB * KS;
+        constexpr int PF = D < 128 ? 1 : (NK < 3 ? NK : 3);
+        auto read_k = [&](int i) {
+            return __builtin_bit_cast(
+                x8, *reinterpret_cast<const u32x4 *>(smem + KOFF + (i / KS) * 32 * ROW + koff[i % KS]));
+        };
+        auto read_v = [&](int i) {
+            return __builtin_bit_cast(
+                x8, *reinterpret_cast<const u32x4 *>(smem + VOFF + (i / KS) * 32 * ROW + voff[i % KS]));
+        };
+        x8 kq[PF], vq[PF];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int i = 0; i < PF; ++i) {
+            kq[i] = read_k(i);
+            vq[i] = read_v(i);
+        }
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const x8 kf = __builtin_bit_cast(
-                    x8, *reinterpret_cast<const u32x4 *>(smem + KOFF + kb * 32 * ROW + koff[ks]));
-                const x8 vf = __builtin_bit_cast(
-                    x8, *reinterpret_cast<const u32x4 *>(smem + VOFF + kb * 32 * ROW + voff[ks]));
-                s[kb] = M::run(kf, qf[ks], s[kb]);
-                dp[kb] = M::run(vf, dof[ks], dp[kb]);
+        for (int i = 0; i < NK; ++i) {
+            const x8 kf = kq[i % PF], vf = vq[i % PF];
+            if (i + PF < NK) {
+                kq[i % PF] = read_k(i + PF);
+                vq[i % PF] = read_v(i + PF);
             }
+            s[i / KS] = M::run(kf, qf[i % KS], s[i / KS]);
+            dp[i / KS] = M::run(vf, dof[i % KS], dp[i / KS]);
+        }
+        if constexpr (PF > 1) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
+#pragma unroll
+            for (int i = 0; i < NK; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                if (i + PF < NK) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+        }
         // ---- mask: ragged key tail and the causal diagonal (P = exp2(-inf) = 0;
         // dP is finite, so dS = 0 there too) ---------------------------------------
         const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > q0w);
