@@ -35,6 +35,15 @@
  * returns; results are valid once the stream has completed that work.  A
  * NULL stream is the device's default (null) stream.
  *
+ * Graph capture.  No kernel clears memory with a memset, so every entry
+ * point may be captured into a HIP graph on ``stream`` and replayed.  The
+ * split workspace of ``fa_fwd`` is allocated (hipMalloc) by the first call
+ * on a stream that needs it: make one such call on the capturing stream
+ * before capture.  A captured ``fa_fwd`` holds that workspace's address, so
+ * while the graph is in use do not call ``fa_release_workspace`` or an
+ * ``fa_fwd`` needing a larger workspace on that stream; the entry points
+ * that take a caller workspace have no such constraint.
+ *
  * Errors.  Entry points return an ``fa_status``.  All arguments are checked
  * on the host before any HIP call, so a rejected call has no device side
  * effects.  ``fa_last_error`` returns a message for the calling thread's
