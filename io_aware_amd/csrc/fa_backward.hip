@@ -479,6 +479,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
         constexpr int DOOFF = QOFF + TILE_BYTES;
         constexpr int SOFF = QOFF + ST_OFF;
         // ---- S = Q K^T, dP = dO V^T ------------------------------------------
+        // (issued at raised wave priority so that co-resident waves stay out
+        // of step: one wave's exponentials run beside another's MFMAs)
+        __builtin_amdgcn_s_setprio(1);
         f32x16 s[QB], dp[QB];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -503,6 +506,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
                     dp[qb] = M::run(da, vf[ks], dp[qb]);
                 }
             }
+        __builtin_amdgcn_s_setprio(0);
         // ---- mask: ragged query tail and the causal diagonal (P = exp2(-inf) =
         // 0; dP and the tile's statistics are finite, so dS = 0 there too) ----------
         // register r of query block qb is query qt + 32*qb + acc_row(r, g);

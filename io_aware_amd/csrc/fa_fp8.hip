@@ -526,6 +526,9 @@ void fp8_fwd_kernel(Fp8Args a) {
         constexpr int S = decltype(stage_tag)::value;
         const char *base = smem + S * STAGE;
         // ---- S^T = K Q^T ------------------------------------------------------
+        // (issued at raised wave priority, as in the 16-bit prefill kernel, so
+        // that co-resident waves stay out of step)
+        __builtin_amdgcn_s_setprio(1);
         f32x16 s[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -539,6 +542,7 @@ void fp8_fwd_kernel(Fp8Args a) {
                 s[kb] = mfma_e4m3(kf, qf[ks], s[kb]);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         // ---- mask: key tail and the causal diagonal -----------------------------
         const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > q0w);
         if (need_mask) {

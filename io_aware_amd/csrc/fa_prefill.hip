@@ -30,6 +30,9 @@
 //  * Registers are budgeted for two waves per SIMD: a CU holds two
 //    independent workgroups whose MFMA and softmax phases overlap.
 //  * exp is computed as exp2 with scale*log2(e) folded into one FMA.
+//  * Each wave raises its priority (s_setprio) while it issues the S^T
+//    MFMA chain and drops it for the softmax and P V, which keeps the
+//    co-resident waves of a SIMD in different phases.
 //  * Lazy rescale: P is formed against the max the row is held at; the
 //    accumulator is rescaled (and the held max moved to the exact running
 //    max) only when some lane's tile sum of P exceeds 2^8.  Until then every
@@ -251,6 +254,10 @@ void prefill_kernel(PrefillArgs a) {
         constexpr int KOFF = S * STAGE_BYTES;
         constexpr int VOFF = KOFF + TILE_BYTES;
         // ---- S^T = K_blk Q^T -------------------------------------------------
+        // The wave runs at raised priority while it issues this chain, so
+        // that co-resident waves of other workgroups fall out of step with
+        // it: one wave's exponentials then run beside another's MFMAs.
+        __builtin_amdgcn_s_setprio(1);
         f32x16 s[QB][KB];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -286,6 +293,8 @@ void prefill_kernel(PrefillArgs a) {
                 if (i + KPF < NK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
         }
+
+        __builtin_amdgcn_s_setprio(0);
 
         // ---- mask: ragged key tail and the causal diagonal ------------------
         const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > q0w);
@@ -323,7 +332,9 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         t[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][h + e], c, -msub));
-                        lsum += t[e];
+                        // start the sum from the first term: 0 + x cannot be
+                        // folded away in IEEE arithmetic (x = -0), and P >= 0
+                        lsum = (ks2 == 0 && e == 0) ? t[e] : lsum + t[e];
                     }
                     pf[qb][ks2] = __builtin_convertvector(t, x8);
                 }
