@@ -35,14 +35,20 @@
  * returns; results are valid once the stream has completed that work.  A
  * NULL stream is the device's default (null) stream.
  *
+ * Threads.  Every entry point may be called from several host threads at
+ * once.  The only state shared between calls is the workspace cache of
+ * ``fa_fwd``, guarded by a mutex; the error message is per thread.
+ *
  * Graph capture.  No kernel clears memory with a memset, so every entry
  * point may be captured into a HIP graph on ``stream`` and replayed.  The
  * split workspace of ``fa_fwd`` is allocated (hipMalloc) by the first call
  * on a stream that needs it: make one such call on the capturing stream
- * before capture.  A captured ``fa_fwd`` holds that workspace's address, so
- * while the graph is in use do not call ``fa_release_workspace`` or an
- * ``fa_fwd`` needing a larger workspace on that stream; the entry points
- * that take a caller workspace have no such constraint.
+ * before capture.  A captured ``fa_fwd`` holds that workspace's address.  A
+ * later call that needs a larger workspace on that stream allocates a new
+ * one and keeps the old one alive, so the graph stays valid; only
+ * ``fa_release_workspace`` frees them, so do not call it while the graph is
+ * in use.  The entry points that take a caller workspace have no such
+ * constraint.
  *
  * Errors.  Entry points return an ``fa_status``.  All arguments are checked
  * on the host before any HIP call, so a rejected call has no device side
@@ -289,8 +295,10 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *out,
 int fa_default_num_splits(int Nk);
 
 /*
- * fa_release_workspace -- waits for the streams that used them, then frees
- * the workspaces fa_fwd allocated.  Returns FA_OK or FA_ERR_HIP.
+ * fa_release_workspace -- waits for the devices that used them, then frees
+ * every workspace fa_fwd allocated, including those replaced by larger ones
+ * (a workspace that grows is never freed in place, since work enqueued
+ * earlier may still use it).  Returns FA_OK or FA_ERR_HIP.
  */
 int fa_release_workspace(void);
 

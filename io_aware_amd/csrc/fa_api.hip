@@ -10,6 +10,7 @@
 #include <mutex>
 #include <string>
 #include <utility>
+#include <vector>
 
 #include "fa.h"
 #include "fa_internal.h"
@@ -90,13 +91,18 @@ int prefill_shape(int d) {
 }
 
 // Library-owned split workspaces (decode, and split prefill), one per
-// (device, stream).
+// (device, stream).  A workspace that must grow is replaced, never freed in
+// place: work enqueued earlier (by this or another thread, or a captured
+// graph) may still use the old buffer, so it is retired and freed only by
+// fa_release_workspace.  Growth is geometric, so the retired buffers of a
+// stream together are smaller than its live one.
 struct Workspace {
     void *ptr = nullptr;
     size_t bytes = 0;
 };
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+std::vector<std::pair<int, void *>> g_retired;  // (device, buffer)
 
 int get_workspace(size_t need, hipStream_t stream, void **out) {
     int dev = 0;
@@ -105,21 +111,21 @@ int get_workspace(size_t need, hipStream_t stream, void **out) {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace &w = g_ws[std::make_pair(dev, stream)];
     if (w.bytes < need) {
-        if (w.ptr) {
-            // earlier work on this stream may still read the old buffer
-            err = hipStreamSynchronize(stream);
-            if (err != hipSuccess) return hip_status(err, "hipStreamSynchronize");
-            err = hipFree(w.ptr);
-            w.ptr = nullptr;
-            w.bytes = 0;
-            if (err != hipSuccess) return hip_status(err, "hipFree");
+        size_t bytes = w.bytes > need / 2 ? 2 * w.bytes : need;
+        void *p = nullptr;
+        err = hipMalloc(&p, bytes);
+        if (err != hipSuccess && bytes > need) {  // the doubled size did not fit: take what is needed
+            (void)hipGetLastError();              // clear the failed allocation's error
+            bytes = need;
+            err = hipMalloc(&p, bytes);
         }
-        err = hipMalloc(&w.ptr, need);
         if (err != hipSuccess) {
-            w.ptr = nullptr;
+            (void)hipGetLastError();
             return hip_status(err, "hipMalloc(workspace)");
         }
-        w.bytes = need;
+        if (w.ptr) g_retired.emplace_back(dev, w.ptr);
+        w.ptr = p;
+        w.bytes = bytes;
     }
     *out = w.ptr;
     return FA_OK;
@@ -429,6 +435,13 @@ int fa_release_workspace(void) {
         kv.second.bytes = 0;
     }
     g_ws.clear();
+    for (auto &r : g_retired) {
+        hipError_t err = hipSetDevice(r.first);
+        if (err == hipSuccess) err = hipDeviceSynchronize();
+        if (err == hipSuccess) err = hipFree(r.second);
+        if (err != hipSuccess) status = hip_status(err, "releasing a workspace");
+    }
+    g_retired.clear();
     if (have_prev) (void)hipSetDevice(prev);
     return status == FA_OK ? ok() : status;
 }

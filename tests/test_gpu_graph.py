@@ -79,6 +79,41 @@ def test_forward_in_a_graph(fa, B, H, Nq, Nk, d, causal):
                       lambda s: fa_inputs.make_qkv_device(B, H, Nq, Nk, d, "bf16", seed=s, device=DEV))
 
 
+def test_graph_survives_workspace_growth(fa):
+    """A captured decode holds its stream's library workspace.  A later call
+    on that stream that needs a larger workspace gets a new one; the old one
+    stays allocated, so replays of the graph stay correct."""
+    B, H, Nk, d = 2, 4, 1024, 128
+    q, k, v = fa_inputs.make_qkv_device(B, H, 1, Nk, d, "bf16", seed=44, device=DEV)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, 1), dtype=torch.float32, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fa.fa_fwd(q, k, v, out=out, lse=lse)       # allocates the side stream's workspace
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        fa.fa_fwd(q, k, v, out=out, lse=lse)
+    torch.cuda.synchronize()
+    # a decode with 32x the rows and 8x the keys on the same stream: its
+    # workspace does not fit in the captured one, which is replaced
+    qb, kb, vb = fa_inputs.make_qkv_device(8, 16, 1, 8192, d, "bf16", seed=45, device=DEV)
+    side.wait_stream(torch.cuda.current_stream())   # the inputs were drawn on the current stream
+    with torch.cuda.stream(side):
+        big_out, big_lse = fa.fa_fwd(qb, kb, vb)
+    torch.cuda.synchronize()
+    want_o, want_l = fa.fa_fwd(qb, kb, vb)
+    torch.cuda.synchronize()
+    assert torch.equal(big_out, want_o) and torch.equal(big_lse, want_l)
+
+    def eager():
+        return fa.fa_fwd(q, k, v)
+
+    _replay_and_check(fa, g, (q, k, v), (out, lse), eager, (46, 47),
+                      lambda s: fa_inputs.make_qkv_device(B, H, 1, Nk, d, "bf16", seed=s, device=DEV))
+
+
 def test_varlen_in_a_graph(fa):
     H, d = 4, 64
     lens = [700, 1, 333, 0, 1024, 65]
