@@ -145,7 +145,8 @@ def test_default_num_splits(fa):
     assert fa.fa_default_num_splits(0) == 0
 
 
-@pytest.mark.parametrize("BH,Tr", [(128, 32), (32, 128), (16, 8), (3, 5), (1, 1), (512, 1)])
+@pytest.mark.parametrize("BH,Tr", [(128, 32), (32, 128), (16, 8), (3, 5), (1, 1), (512, 1), (24, 33), (8, 3),
+                                   (136, 7)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_workgroup_order_is_a_bijection(fa, BH, Tr, causal):
     seen = set()
@@ -167,6 +168,34 @@ def test_workgroup_order_groups_heads_by_xcd(fa):
     # causal: the first workgroup of a head takes its last (longest) block
     assert fa.fa_map_workgroup(0, BH, Tr, True) == (0, Tr - 1)
     assert fa.fa_map_workgroup(0, BH, Tr, False) == (0, 0)
+
+
+@pytest.mark.parametrize("BH,Tr", [(128, 32), (512, 16), (32, 128), (24, 33), (8, 3)])
+def test_causal_order_phases_and_head_groups(fa, BH, Tr):
+    """Causal order on each XCD: first the Q blocks >= Tr/4 four heads at a
+    time (interleaved, longest first), then the blocks < Tr/4 the same way."""
+    hpx = BH // 8
+    gh = min(4, hpx)
+    while hpx % gh:
+        gh -= 1
+    split = Tr // 4
+    for x in range(8):
+        seq = [fa.fa_map_workgroup(8 * w + x, BH, Tr, True) for w in range(hpx * Tr)]
+        assert all(bh // hpx == x for bh, _ in seq)                    # whole heads per XCD
+        n1 = (Tr - split) * hpx
+        assert all(qb >= split for _, qb in seq[:n1]) and all(qb < split for _, qb in seq[n1:])
+        for lo, hi, part in ((split, Tr, seq[:n1]), (0, split, seq[n1:])):
+            if hi == lo:                                                # Tr < 4: no second phase
+                assert not part
+                continue
+            per_group = (hi - lo) * gh
+            for g0 in range(0, len(part), per_group):
+                grp = part[g0:g0 + per_group]
+                heads = sorted(set(bh for bh, _ in grp))
+                assert len(heads) == gh and heads == list(range(heads[0], heads[0] + gh))
+                blocks = [qb for _, qb in grp]
+                assert blocks == sorted(blocks, reverse=True)           # longest first within the group
+                assert blocks[0] == hi - 1
 
 
 # fake addresses for the paged entry point: caches, table and lengths far apart
