@@ -316,6 +316,31 @@ def test_side_stream(fa, Nq):
     assert t1 >= 0.5 * t_main and t2 >= 0.5 * t_main, (t_main, t1, t2)
 
 
+def test_release_workspace_after_growth(fa):
+    """Grow the library workspace of two streams (the replaced buffers are
+    retired, not freed), release everything, and decode again: the release
+    returns FA_OK twice in a row and later calls allocate afresh and give
+    the same results bit for bit."""
+    side = torch.cuda.Stream()
+    shapes = [(2, 4, 1024), (4, 8, 30000), (8, 16, 8192)]   # split workspaces of 16 KB, 1 MB, 2.1 MB
+    results = {}
+    for B, H, Nk in shapes:
+        q, k, v = fa_inputs.make_qkv_device(B, H, 1, Nk, 128, "bf16", seed=Nk, device=DEV)
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            o_side, l_side = fa.fa_fwd(q, k, v)
+        o, l = fa.fa_fwd(q, k, v)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_side) and torch.equal(l, l_side)
+        results[(B, H, Nk)] = (q, k, v, o, l)
+    fa.fa_release_workspace()   # raises FAError unless FA_OK
+    fa.fa_release_workspace()
+    for (B, H, Nk), (q, k, v, o, l) in results.items():
+        o2, l2 = fa.fa_fwd(q, k, v)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o2) and torch.equal(l, l2)
+
+
 def test_lse_optional(fa):
     q, k, v = fa_inputs.make_qkv(1, 2, 100, 100, 64, "bf16", seed=26)
     qd, kd, vd = to_dev(q, k, v)
