@@ -45,8 +45,9 @@
 //    only blocks that cross the diagonal or the ragged key tail are masked.
 //    Rows of the ragged key tail are fetched from the last key (finite data
 //    that the mask removes), so no load leaves the tensor.
-//  * Workgroup order: whole heads per XCD, two heads interleaved, longest
-//    causal blocks first (fa_layout.h).
+//  * Workgroup order: whole heads per XCD; under the causal mask the XCD's
+//    heads four at a time in two phases (long blocks, then short), longest
+//    first, which balances the hardware's in-order dispatch (fa_layout.h).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
