@@ -35,11 +35,13 @@
 //    co-resident waves of a SIMD in different phases.
 //  * Lazy rescale: P is formed against the max the row is held at; the
 //    accumulator is rescaled (and the held max moved to the exact running
-//    max) only when some lane's tile sum of P exceeds 2^8.  Until then every
-//    P <= 2^8, which float32 and the 16-bit types hold without loss of
-//    relative precision, and no per-tile row max is needed; O and LSE are the
-//    same function of the inputs because acc, l and m always refer to the
-//    same held max.
+//    max) only when some lane's tile sum of P exceeds 2^15.  Until then every
+//    P <= 2^15, which float32, bf16 and fp16 (largest finite 65504) hold
+//    without loss of relative precision, and no per-tile row max is needed;
+//    O and LSE are the same function of the inputs because acc, l and m
+//    always refer to the same held max.  (With scores of large spread the
+//    running max keeps growing; at 2^8 the exact step ran more often: the
+//    wave takes it when any of its 32 rows needs it.)
 //  * Causal: K/V blocks after a workgroup's last query are never loaded;
 //    a wave skips the MFMA work of blocks entirely after its own last query;
 //    only blocks that cross the diagonal or the ragged key tail are masked.
@@ -93,8 +95,9 @@ constexpr int kModeVarlen = 1;
 constexpr int kModeSplit = 2;
 
 // Bound on a lane's per-tile sum of P between rescales; it keeps every
-// P <= 2^8 (see the online-softmax step of prefill_kernel).
-constexpr float kHeldSumBound = 256.0f;
+// P <= 2^15 (see the online-softmax step of prefill_kernel); fp16 P must
+// stay below 65504.
+constexpr float kHeldSumBound = 32768.0f;
 constexpr float kLn2 = 0.693147180559945309417f;
 
 template <typename T, int D, bool CAUSAL, int NW, int QW, int BC, int OCC, int MODE>
@@ -315,7 +318,7 @@ void prefill_kernel(PrefillArgs a) {
 
         // ---- online softmax -------------------------------------------------
         // P = exp2(c*s - m_held) and its row sums are formed first.  A lane's
-        // tile sum <= 2^8 bounds each of its P by 2^8 (P >= 0), which is the
+        // tile sum <= 2^15 bounds each of its P by 2^15 (P >= 0), which is the
         // lazy-rescale invariant, so the row max is only needed when some lane
         // of the wave exceeds it (or has no held max yet).  Then the exact
         // step runs on the untouched scores: m_new = max(m_held, rowmax),
