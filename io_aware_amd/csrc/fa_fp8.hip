@@ -564,7 +564,8 @@ void fp8_fwd_kernel(Fp8Args a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     t[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[w >> 2][4 * (w & 3) + e], c, -msub));
-                    lsum += t[e];
+                    // from the first term: 0 + x does not fold (x = -0), P >= 0
+                    lsum = (w == 0 && e == 0) ? t[e] : lsum + t[e];
                 }
                 pf[w] = (int)to_e4m3x4(t[0], t[1], t[2], t[3]);
             }
