@@ -34,6 +34,11 @@ struct Mfma<__bf16> {
     static __device__ __forceinline__ f32x16 run(x8 a, x8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
+    // D (16x16, float32) += A (16x32) B (32x16)
+    static __device__ __forceinline__ f32x4 run16(x8 a, x8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    static constexpr uint16_t kOne = 0x3F80;  // 1.0
 };
 
 template <>
@@ -43,6 +48,11 @@ struct Mfma<_Float16> {
     static __device__ __forceinline__ f32x16 run(x8 a, x8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
     }
+    // D (16x16, float32) += A (16x32) B (32x16)
+    static __device__ __forceinline__ f32x4 run16(x8 a, x8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+    static constexpr uint16_t kOne = 0x3C00;  // 1.0
 };
 
 template <int N>

@@ -8,8 +8,9 @@
 //   S = scale * Q K^T (MFMA, float32 accumulate), mask, m_new = max(m, rowmax S),
 //   rescale acc and l by exp(m - m_new), P = exp(S - m_new) rounded to the
 //   input type, l += rowsum P, acc += P V (MFMA);
-// after the last block O = acc / l and LSE = m + ln l.  Score and
-// probability tiles live only in registers.
+// after the last block O = acc / l and LSE = m + ln l, with O normalised by
+// the sum of the rounded P that formed acc (l itself, in float32, gives the
+// LSE).  Score and probability tiles live only in registers.
 //
 // CDNA4 design (index arithmetic in fa_layout.h, checked on the host):
 //  * 32x32x16 bf16/fp16 MFMA in transposed orientation: S^T = K Q^T and
@@ -237,10 +238,31 @@ void prefill_kernel(PrefillArgs a) {
     f32x16 oacc[QB][DB];
     float m_held[QB];
     float l_part[QB];
+    // Two running sums per row: l_part of the float32 P (for LSE and the
+    // lazy-rescale test) and lt of the P rounded to the input type, the
+    // weights P V is formed with; O is normalised by lt, so O is a convex
+    // combination of value rows whatever the rounding of a dominant weight
+    // (which is not 1 while the held max lags the row max).  lt is summed
+    // on the matrix core: read as the B operand of a 16x16x32 product, the
+    // P^T registers of lanes n and n+32 (query n) form K blocks 0 and 2 of
+    // column n, those of lanes n+16 and n+48 (query n+16) K blocks 1 and 3.
+    // With A row 0 = ones on blocks 0, 2 and row 1 = ones on blocks 1, 3
+    // (lanes 0, 32 and 17, 49; every other lane zero), lane n < 16 of the
+    // accumulator holds query n's sum in register 0 and query n+16's in
+    // register 1.
+    f32x4 lt[QB];
+    x8 ones8;
+    {
+        const uint16_t one = (lane == 0 || lane == 32 || lane == 17 || lane == 49) ? M::kOne : (uint16_t)0;
+        const uint32_t w2 = (uint32_t)one * 0x10001u;
+        ones8 = __builtin_bit_cast(x8, u32x4{w2, w2, w2, w2});
+    }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         m_held[qb] = -__builtin_inff();
         l_part[qb] = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lt[qb][r] = 0.0f;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -273,7 +295,7 @@ void prefill_kernel(PrefillArgs a) {
         // (with 64 queries per wave each fragment feeds two MFMAs, which
         // hides the read by itself: the compiler schedules those shapes)
         constexpr int NK = KB * KS;
-        constexpr int KPF = QB > 1 ? 1 : (NK < 4 ? NK : 4);
+        constexpr int KPF = QB > 1 ? 1 : (NK < 3 ? NK : 3);
         auto read_k = [&](int i) {
             return __builtin_bit_cast(
                 x8, *reinterpret_cast<const u32x4 *>(smem + KOFF + (i / KS) * 32 * ROW + koff[i % KS]));
@@ -362,6 +384,10 @@ void prefill_kernel(PrefillArgs a) {
                     (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_held[qb] - m_new);
                 m_held[qb] = m_new;
                 l_part[qb] *= alpha;
+                // lane n < 16 keeps queries n (register 0) and n + 16 (register 1)
+                const float alpha_hi = __shfl(alpha, (lane + 16) & 63);
+                lt[qb][0] *= alpha;
+                lt[qb][1] *= alpha_hi;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha;
                 // a row that has seen no key yet keeps m = -inf: subtract 0
@@ -370,6 +396,12 @@ void prefill_kernel(PrefillArgs a) {
             }
             l_part[qb] += lsum;
         }
+
+        // ---- lt += rowsum of the rounded P (matrix core) -----------------------
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int ks2 = 0; ks2 < KS2; ++ks2) lt[qb] = M::run16(ones8, pf[qb][ks2], lt[qb]);
 
         // ---- O^T += V^T P^T -------------------------------------------------
         // step i = (k-step i / DB, d block i % DB); its V^T fragment (two
@@ -394,6 +426,7 @@ void prefill_kernel(PrefillArgs a) {
             for (int qb = 0; qb < QB; ++qb) oacc[qb][i % DB] = M::run(vf, pf[qb][i / DB], oacc[qb][i % DB]);
         }
         if constexpr (QB == 1) {
+            __builtin_amdgcn_sched_group_barrier(0x008, KS2, 0);  // the row-sum products first
             __builtin_amdgcn_sched_group_barrier(0x100, 2 * VPF, 0);
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
@@ -430,9 +463,12 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const float l = xor32_sum(l_part[qb]);
+        const float lt_lo = __shfl(lt[qb][0], l32 & 15);
+        const float lt_hi = __shfl(lt[qb][1], l32 & 15);
+        const float lw = (l32 < 16) ? lt_lo : lt_hi;  // sum of this row's rounded P
         const int row = q0w + 32 * qb + l32;
         if (row < Nq) {
-            const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
+            const float inv = (l > 0.0f && lw > 0.0f) ? 1.0f / lw : 0.0f;
             const float lse_row = (l > 0.0f) ? (m_held[qb] + __builtin_amdgcn_logf(l)) * kLn2 : -__builtin_inff();
             if constexpr (SPLIT) {
                 const size_t slot = ((size_t)bh * Nq + row) * a.S + chunk_idx;

@@ -60,6 +60,24 @@ def test_ragged_causal_f16(fa):
     run_full(fa, w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.causal, w.seed, label=w.name)
 
 
+@pytest.mark.parametrize("name", ["prefill_causal_bf16_b8h16_n4096_d128", "long_bf16_b1h32_n16384_d128_qsigma8"])
+def test_full_size_prefill_every_row(fa, name):
+    """Every one of the 524288 output rows of the two full-size prefill
+    workloads against the fp64 oracle (about 6 s and 47 s of oracle time on
+    16 cores).  The bound is a maximum over all rows: with large score
+    spread a few hundred thousand rows hold a handful near the limit, which
+    a sample of rows can miss."""
+    w = fa_inputs.WORKLOADS[name]
+    note("case %s (all rows)" % name)
+    q, k, v = fa_inputs.make_workload(w)
+    qd, kd, vd = to_dev(q, k, v)
+    out, lse = fa.fa_fwd(qd, kd, vd, scale=w.scale, causal=w.causal)
+    torch.cuda.synchronize()
+    del qd, kd, vd
+    ref_o, ref_l = oracle.attention(q, k, v, w.scale, w.causal)
+    compare(out, lse, ref_o, ref_l, w.dtype, name)
+
+
 @pytest.mark.parametrize("name,nrows", [("prefill_causal_bf16_b8h16_n4096_d128", 3000),
                                         ("long_bf16_b1h32_n16384_d128_qsigma8", 1500)])
 def test_full_size_prefill_sampled_rows(fa, name, nrows):
