@@ -397,12 +397,6 @@ void prefill_kernel(PrefillArgs a) {
             l_part[qb] += lsum;
         }
 
-        // ---- lt += rowsum of the rounded P (matrix core) -----------------------
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int ks2 = 0; ks2 < KS2; ++ks2) lt[qb] = M::run16(ones8, pf[qb][ks2], lt[qb]);
-
         // ---- O^T += V^T P^T -------------------------------------------------
         // step i = (k-step i / DB, d block i % DB); its V^T fragment (two
         // transposing reads) is read VPF steps ahead of its MFMA (at 32
@@ -425,14 +419,19 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) oacc[qb][i % DB] = M::run(vf, pf[qb][i / DB], oacc[qb][i % DB]);
         }
+        // ---- lt += rowsum of the rounded P (matrix core), after P V -------------
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int ks2 = 0; ks2 < KS2; ++ks2) lt[qb] = M::run16(ones8, pf[qb][ks2], lt[qb]);
         if constexpr (QB == 1) {
-            __builtin_amdgcn_sched_group_barrier(0x008, KS2, 0);  // the row-sum products first
             __builtin_amdgcn_sched_group_barrier(0x100, 2 * VPF, 0);
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 if (i + VPF < NV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x008, KS2, 0);
         }
     };
 
