@@ -18,7 +18,10 @@
  * contiguous row-major (d fastest) in the element type ``dtype``.
  * lse: [B, H, Nq] float32.  Accumulation and the m/l statistics are float32
  * on every path; probabilities are rounded to the input type (nearest-even)
- * before the P.V product, and O is rounded to the input type (nearest-even).
+ * before the P.V product, O is divided by the sum of those rounded
+ * probabilities (a convex combination of value rows) while LSE comes from
+ * the float32 sum, and O is rounded to the input type (nearest-even).
+ * (The single-token split-KV path keeps its probabilities in float32.)
  *
  * Causal mask (``causal`` = 1): key j is visible to query i iff j <= i
  * (top-left alignment, for any Nq and Nk; "6. FlashAttention 分块逻辑",
