@@ -78,8 +78,9 @@ typedef enum fa_dtype {
 /* Status codes. */
 typedef enum fa_status {
     FA_OK = 0,
-    FA_ERR_INVALID_ARG = 1,  /* null pointer, a size < 1, scale not finite and > 0,
-                                causal not 0/1, overlapping outputs, num_splits < 1 */
+    FA_ERR_INVALID_ARG = 1,  /* null pointer, a size < 1, scale not finite (or
+                                |scale|*log2(e) past float32 range), causal not
+                                0/1, overlapping outputs, num_splits < 1 */
     FA_ERR_UNSUPPORTED = 2,  /* d not in {32, 64, 128}, unknown dtype, a pointer not
                                 16-byte aligned (lse: 4-byte), sizes past the index
                                 range, or a shape the entry point does not take */
@@ -92,8 +93,11 @@ typedef enum fa_status {
  *
  * q, k, v, out: device pointers as described above; lse: device pointer to
  * [B, H, Nq] float32, or NULL to skip writing LSE.  B, H, Nq, Nk >= 1;
- * d in {32, 64, 128}; scale finite and > 0 (normally 1/sqrt(d)); causal 0 or
- * 1; dtype an fa_dtype.
+ * d in {32, 64, 128}; causal 0 or 1; dtype an fa_dtype.  scale: the
+ * caller's softmax scale (normally 1/sqrt(d); "08. Triton Flash Attention",
+ * the exercise's sm_scale), any finite value whose product with log2(e) is
+ * a finite float32, negative and zero included (a zero scale gives every
+ * visible key the same weight); this holds for every entry point below.
  *
  * Dispatch: Nq == 1 without the mask (single-token decode) runs the split-KV
  * path ("6. FlashAttention 分块逻辑", section 11: K/V split into chunks that

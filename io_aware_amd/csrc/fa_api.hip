@@ -42,6 +42,13 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 
 size_t element_size(int dtype) { return dtype == FA_F32 ? 4 : 2; }
 
+// Any finite scale whose product with log2(e) is a finite float32 (the
+// kernels work in base 2); negative and zero scales included.
+bool scale_ok(float scale) {
+    return std::isfinite(scale) && std::isfinite((float)((double)scale * kLog2e));
+}
+constexpr const char *kScaleMsg = "scale must be finite, with |scale| * log2(e) within float32 range";
+
 // Checks shared by every forward entry point.  Returns FA_OK or the status
 // to return, with the message set.
 int check_common(const void *q, const void *k, const void *v, const void *out, const float *lse, int B, int H,
@@ -49,7 +56,7 @@ int check_common(const void *q, const void *k, const void *v, const void *out, c
     if (!q || !k || !v || !out) return fail(FA_ERR_INVALID_ARG, "q, k, v and out must be non-null");
     if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1)
         return fail(FA_ERR_INVALID_ARG, "B, H, Nq, Nk and d must all be >= 1");
-    if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+    if (!scale_ok(scale)) return fail(FA_ERR_INVALID_ARG, kScaleMsg);
     if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16)
         return fail(FA_ERR_UNSUPPORTED, "dtype must be FA_F32 (0), FA_F16 (1) or FA_BF16 (2)");
     if (d != 32 && d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "d must be 32, 64 or 128");
@@ -208,7 +215,7 @@ int fa_fwd_paged_decode(const void *q, const void *k_cache, const void *v_cache,
         return fail(FA_ERR_INVALID_ARG, "q, k_cache, v_cache, block_table, seq_lens and out must be non-null");
     if (B < 1 || H < 1 || d < 1 || block_size < 1 || max_blocks < 1 || num_blocks < 1)
         return fail(FA_ERR_INVALID_ARG, "B, H, d, block_size, max_blocks_per_seq and num_blocks must be >= 1");
-    if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+    if (!scale_ok(scale)) return fail(FA_ERR_INVALID_ARG, kScaleMsg);
     if (num_splits < 1 || num_splits > kMaxSplits)
         return fail(FA_ERR_INVALID_ARG, "num_splits must be in [1, 1024]");
     if (dtype != FA_F16 && dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "the paged path takes fp16 or bf16");
@@ -316,7 +323,7 @@ int fa_fwd_varlen(const void *q, const void *k, const void *v, void *out, float 
         return fail(FA_ERR_INVALID_ARG, "q, k, v, out, cu_seqlens_q and cu_seqlens_k must be non-null");
     if (num_seqs < 1 || total_q < 1 || total_k < 1 || H < 1 || d < 1)
         return fail(FA_ERR_INVALID_ARG, "num_seqs, total_q, total_k, H and d must be >= 1");
-    if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+    if (!scale_ok(scale)) return fail(FA_ERR_INVALID_ARG, kScaleMsg);
     if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
     if (dtype != FA_F16 && dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "the variable-length path takes fp16 or bf16");
     if (d != 32 && d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "d must be 32, 64 or 128");
@@ -398,7 +405,7 @@ int fa_fwd_fp8(const void *pack, void *out, float *lse, int B, int H, int Nq, in
     if (!pack || !out) return fail(FA_ERR_INVALID_ARG, "pack and out must be non-null");
     int st = check_fp8_sizes(B, H, Nq, Nk, d);
     if (st != FA_OK) return st;
-    if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+    if (!scale_ok(scale)) return fail(FA_ERR_INVALID_ARG, kScaleMsg);
     if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
     if (out_dtype != FA_F16 && out_dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "out must be fp16 or bf16");
     if (!aligned(pack, 256) || !aligned(out, 16) || (lse && !aligned(lse, 4)))

@@ -62,8 +62,10 @@ struct BwdArgs {
     int Nq;
     int Nk;
     int T;              // blocks per (batch, head): Q blocks (dQ kernel) or K blocks (dK/dV kernel)
-    float scale;
-    float scale_log2;   // scale * log2(e)
+    float scale;        // the caller's scale (dQ = scale dS K, dK = scale dS^T Q)
+    float scale_log2;   // |scale| * log2(e) (1 for a zero scale; see FoldedScale)
+    uint32_t sflip;     // sign bits flipped in the register-held score operand (Q in
+    uint32_t skeep;     // the dQ kernel, K in the dK/dV kernel); 0 zeroes it
 };
 
 // ---------------------------------------------------------------------------
@@ -173,7 +175,7 @@ void bwd_dq_kernel(BwdArgs a) {
             rdo = *reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.dout) + off);
             ro = *reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.out) + off);
         }
-        qf[ks] = __builtin_bit_cast(x8, rq);
+        qf[ks] = __builtin_bit_cast(x8, (rq ^ a.sflip) & a.skeep);  // the scale's sign, folded into Q
         dof[ks] = __builtin_bit_cast(x8, rdo);
         const x8 of = __builtin_bit_cast(x8, ro);
 #pragma unroll
@@ -437,7 +439,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
         const T *vp = static_cast<const T *>(a.v) + ((size_t)bh * Nk + key_c) * D;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            kf[ks] = __builtin_bit_cast(x8, *reinterpret_cast<const u32x4 *>(kp + 16 * ks + 8 * g));
+            // the sign of the scale, folded into K (K serves only S = Q K^T here)
+            kf[ks] = __builtin_bit_cast(x8, (*reinterpret_cast<const u32x4 *>(kp + 16 * ks + 8 * g) ^ a.sflip) &
+                                                a.skeep);
             if constexpr (!VLDS)
                 vf[ks] = __builtin_bit_cast(x8, *reinterpret_cast<const u32x4 *>(vp + 16 * ks + 8 * g));
             voff[ks] = VT_OFF + layout::k_operand_offset<D>(wave, l32, g, ks);
@@ -679,7 +683,10 @@ hipError_t launch_backward(int dtype, int d, bool causal, const void *q, const v
     a.Nq = Nq;
     a.Nk = Nk;
     a.scale = scale;
-    a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+    const FoldedScale fs = fold_scale((float)((double)scale * 1.4426950408889634074), kSignBits16);
+    a.scale_log2 = fs.c;
+    a.sflip = fs.flip;
+    a.skeep = fs.keep;
     if (dtype == 2) return launch_bwd_d<__bf16>(d, causal, a, stream);
     if (dtype == 1) return launch_bwd_d<_Float16>(d, causal, a, stream);
     return hipErrorInvalidValue;

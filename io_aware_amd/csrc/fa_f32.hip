@@ -36,7 +36,9 @@ struct F32Args {
     int Nq;
     int Nk;
     int Tr;  // 64-row Q blocks per (batch, head)
-    float scale_log2;
+    float scale_log2;  // |scale| * log2(e) (1 for a zero scale; see FoldedScale)
+    uint32_t qflip;    // sign bit flipped in Q for a negative scale
+    uint32_t qkeep;    // 0 zeroes Q for a zero scale
 };
 
 // waves per workgroup: as many as keep q and o (2 D floats per lane) in
@@ -77,6 +79,8 @@ __global__ __launch_bounds__(f32_waves<D>() * 64) void prefill_f32_kernel(F32Arg
     for (int t = 0; t < D; t += 4) {
         f32x4 x = {0.f, 0.f, 0.f, 0.f};
         if (row < Nq) x = *reinterpret_cast<const f32x4 *>(qp + (size_t)row * D + t);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = __uint_as_float((__float_as_uint(x[e]) ^ a.qflip) & a.qkeep);
         q[t] = x[0];
         q[t + 1] = x[1];
         q[t + 2] = x[2];
@@ -121,7 +125,7 @@ __global__ __launch_bounds__(f32_waves<D>() * 64) void prefill_f32_kernel(F32Arg
             s[jj] = visible ? dot : -__builtin_inff();
             mx = __builtin_fmaxf(mx, s[jj]);
         }
-        const float m_new = __builtin_fmaxf(m, mx * c);
+        const float m_new = __builtin_fmaxf(m, mx * c);  // c > 0 (the sign is in Q)
         const float alpha = (m_new == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
         const float msub = (m_new == -__builtin_inff()) ? 0.f : m_new;
         l *= alpha;
@@ -193,7 +197,10 @@ hipError_t launch_f32_one(const void *q, const void *k, const void *v, void *out
     a.Nq = Nq;
     a.Nk = Nk;
     a.Tr = (Nq + 63) / 64;
-    a.scale_log2 = sl;
+    const FoldedScale fs = fold_scale(sl, kSignBits32);
+    a.scale_log2 = fs.c;
+    a.qflip = fs.flip;
+    a.qkeep = fs.keep;
     const long long nwg = (long long)BH * a.Tr;
     if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((prefill_f32_kernel<D, CAUSAL>), dim3((unsigned)nwg), dim3(f32_waves<D>() * 64), 0, stream, a);

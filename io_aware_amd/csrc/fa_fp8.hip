@@ -365,7 +365,9 @@ struct Fp8Args {
     int Nk;
     int Nkp;
     int Tr;
-    float scale_log2;
+    float scale_log2;  // |scale| * log2(e) (1 for a zero scale; see FoldedScale)
+    uint32_t qflip;    // sign bits flipped in the Q codes for a negative scale
+    uint32_t qkeep;    // 0 zeroes the Q codes for a zero scale
 };
 
 constexpr float kHeldSumBound = 256.0f;
@@ -491,6 +493,8 @@ void fp8_fwd_kernel(Fp8Args a) {
             lo = *reinterpret_cast<const u32x4 *>(p);
             hi = *reinterpret_cast<const u32x4 *>(p + 16);
         }
+        lo = (lo ^ a.qflip) & a.qkeep;  // the sign of the scale, folded into Q
+        hi = (hi ^ a.qflip) & a.qkeep;
         qf[ks] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 
@@ -584,7 +588,7 @@ void fp8_fwd_kernel(Fp8Args a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[kb][r]);
             mx = xor32_max(mx);
-            const float m_new = __builtin_fmaxf(m_held, mx * c);  // c > 0
+            const float m_new = __builtin_fmaxf(m_held, mx * c);  // c > 0 (the sign is in Q)
             const float alpha = (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_held - m_new);
             m_held = m_new;
             l_part *= alpha;
@@ -730,7 +734,10 @@ hipError_t launch_fp8_fwd(int out_dtype, int d, bool causal, const void *pack, v
     a.Nk = Nk;
     a.Nkp = L.Nkp;
     a.Tr = 0;
-    a.scale_log2 = scale_log2;
+    const FoldedScale fs = fold_scale(scale_log2, kSignBits8);
+    a.scale_log2 = fs.c;
+    a.qflip = fs.flip;
+    a.qkeep = fs.keep;
 #define FA_FP8_CASE(OT)                                                                         \
     if (d == 128) return causal ? fwd_typed<OT, 128, true>(a, stream) : fwd_typed<OT, 128, false>(a, stream); \
     return causal ? fwd_typed<OT, 64, true>(a, stream) : fwd_typed<OT, 64, false>(a, stream);

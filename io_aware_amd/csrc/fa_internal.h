@@ -5,8 +5,32 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace fa {
+
+// The softmax scale with its sign folded into one operand of the score
+// product.  scale * (k . q) = |scale| * (k . (-q)) holds exactly: negation
+// only flips sign bits, and products and nearest-even rounded sums are odd
+// functions.  So the kernels always see a positive exp2 factor (they take
+// the row max before scaling) and flip the sign bits of the register-held
+// operand (Q in the forward and the dQ kernel, K in the dK/dV kernel) when
+// the scale is negative.  A zero scale (either sign) zeroes that operand and
+// uses the factor 1: every visible score is then exactly 0, as 0 * (k . q)
+// is, while masked scores stay -inf (-inf * 0 would be NaN).
+struct FoldedScale {
+    float c;        // exp2 factor, > 0
+    uint32_t flip;  // XORed into every 32-bit word of the folded operand
+    uint32_t keep;  // ANDed into every 32-bit word (0 for a zero scale)
+};
+constexpr uint32_t kSignBits16 = 0x80008000u;  // two 16-bit elements per word
+constexpr uint32_t kSignBits8 = 0x80808080u;   // four E4M3 codes per word
+constexpr uint32_t kSignBits32 = 0x80000000u;  // one float32 per word
+inline FoldedScale fold_scale(float c, uint32_t sign_bits) {
+    if (c > 0.0f) return {c, 0u, ~0u};
+    if (c < 0.0f) return {-c, sign_bits, ~0u};
+    return {1.0f, 0u, 0u};
+}
 
 // Prefill tile shapes the library is built with.  A shape is (waves per
 // workgroup, queries per wave, keys per K/V tile); queries per workgroup

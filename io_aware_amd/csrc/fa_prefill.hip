@@ -30,7 +30,9 @@
 //    instruction immediates; per-lane address parts are computed once.
 //  * Registers are budgeted for two waves per SIMD: a CU holds two
 //    independent workgroups whose MFMA and softmax phases overlap.
-//  * exp is computed as exp2 with scale*log2(e) folded into one FMA.
+//  * exp is computed as exp2 with |scale|*log2(e) folded into one FMA; the
+//    sign of the scale is folded into Q (FoldedScale), so the row max can be
+//    taken before scaling.
 //  * Each wave raises its priority (s_setprio) while it issues the S^T
 //    MFMA chain and drops it for the softmax and P V, which keeps the
 //    co-resident waves of a SIMD in different phases.
@@ -73,7 +75,9 @@ struct PrefillArgs {
     int Nq;
     int Nk;
     int Tr;            // Q row blocks per (batch, head)
-    float scale_log2;  // scale * log2(e)
+    float scale_log2;  // |scale| * log2(e) (1 for a zero scale; see FoldedScale)
+    uint32_t qflip;    // sign bits flipped in Q for a negative scale
+    uint32_t qkeep;    // 0 zeroes Q for a zero scale
     // packed variable-length batches (q [total_q, H, d], k and v
     // [total_k, H, d], lse [H, total_q]; the tile list from the schedule)
     const int *cu_q;
@@ -234,6 +238,7 @@ void prefill_kernel(PrefillArgs a) {
         for (int ks = 0; ks < KS; ++ks) {
             u32x4 raw = {0u, 0u, 0u, 0u};
             if (row < Nq) raw = *reinterpret_cast<const u32x4 *>(qp + (size_t)row * RS + 16 * ks + 8 * g);
+            raw = (raw ^ a.qflip) & a.qkeep;  // the sign of the scale, folded into Q
             qf[qb][ks] = __builtin_bit_cast(x8, raw);
         }
     }
@@ -382,7 +387,7 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[qb][kb][r]);
                 mx = xor32_max(mx);
-                const float m_new = __builtin_fmaxf(m_held[qb], mx * c);  // c > 0
+                const float m_new = __builtin_fmaxf(m_held[qb], mx * c);  // c > 0 (the sign is in Q)
                 const float alpha =
                     (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_held[qb] - m_new);
                 m_held[qb] = m_new;
@@ -675,6 +680,13 @@ hipError_t launch_typed(int d, bool causal, int shape, const PrefillArgs &a, boo
 #undef FA_CASE
 }
 
+void set_scale(PrefillArgs &a, float scale_log2) {
+    const FoldedScale fs = fold_scale(scale_log2, kSignBits16);
+    a.scale_log2 = fs.c;
+    a.qflip = fs.flip;
+    a.qkeep = fs.keep;
+}
+
 hipError_t launch_any(int dtype, int d, bool causal, int shape, const PrefillArgs &a, bool varlen, int S,
                       hipStream_t stream) {
     if (dtype == 2) return launch_typed<__bf16>(d, causal, shape, a, varlen, S, stream);
@@ -754,7 +766,7 @@ hipError_t launch_prefill_split(int dtype, int d, bool causal, int shape, const 
     a.BH = BH;
     a.Nq = Nq;
     a.Nk = Nk;
-    a.scale_log2 = scale_log2;
+    set_scale(a, scale_log2);
     a.S = S;
     a.chunk = (key_tiles + S - 1) / S * bc;
     a.ws_o = static_cast<float *>(workspace);
@@ -780,7 +792,7 @@ hipError_t launch_prefill(int dtype, int d, bool causal, int shape, const void *
     a.BH = BH;
     a.Nq = Nq;
     a.Nk = Nk;
-    a.scale_log2 = scale_log2;
+    set_scale(a, scale_log2);
     return launch_any(dtype, d, causal, shape, a, false, 0, stream);
 }
 
@@ -794,7 +806,7 @@ hipError_t launch_prefill_varlen(int dtype, int d, bool causal, int shape, const
     a.v = v;
     a.out = out;
     a.lse = lse;
-    a.scale_log2 = scale_log2;
+    set_scale(a, scale_log2);
     a.cu_q = cu_q;
     a.cu_k = cu_k;
     a.sched = static_cast<const int *>(workspace);

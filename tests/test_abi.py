@@ -80,8 +80,8 @@ def call_fwd(fa, **over):
 @pytest.mark.parametrize("over,code", [
     (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(out=None), 1),
     (dict(B=0), 1), (dict(H=-1), 1), (dict(Nq=0), 1), (dict(Nk=0), 1), (dict(d=0), 1),
-    (dict(scale=0.0), 1), (dict(scale=-0.5), 1), (dict(scale=math.nan), 1), (dict(scale=math.inf), 1),
-    (dict(causal=2), 1), (dict(causal=-1), 1),
+    (dict(scale=math.nan), 1), (dict(scale=math.inf), 1), (dict(scale=-math.inf), 1), (dict(scale=3e38), 1),
+    (dict(scale=-3e38), 1), (dict(causal=2), 1), (dict(causal=-1), 1),
     (dict(dtype=3), 2), (dict(dtype=-1), 2),
     (dict(d=48), 2), (dict(d=256), 2), (dict(d=16), 2),
     (dict(q=Q + 8), 2), (dict(out=O + 4), 2), (dict(lse=L + 2), 2),
@@ -91,6 +91,19 @@ def call_fwd(fa, **over):
 def test_fwd_rejects_invalid_arguments(fa, over, code):
     assert call_fwd(fa, **over) == code
     assert fa.fa_last_error() != ""
+
+
+@pytest.mark.parametrize("scale", [-0.125, 0.0, -0.0, 1e-30, -2.3e38, 2.3e38])
+def test_every_finite_scale_passes_validation(fa, scale):
+    # the scale check runs before the head-dim check: an accepted scale
+    # leaves the call to be rejected for d = 48 (unsupported), not for scale
+    assert call_fwd(fa, scale=scale, d=48) == 2
+    assert "d must be" in fa.fa_last_error()
+    assert call_split(fa, scale=scale, d=48) == 2
+    assert call_paged(fa, scale=scale, d=48) == 2
+    assert call_bwd(fa, scale=scale, d=48) == 2
+    assert call_varlen(fa, scale=scale, d=48) == 2
+    assert call_fwd_fp8(fa, scale=scale, dtype=0) == 2   # its size checks come first: reject the out type
 
 
 def test_error_message_is_per_thread(fa):
@@ -217,7 +230,7 @@ def call_paged(fa, ws_bytes=None, **over):
 @pytest.mark.parametrize("over,code", [
     (dict(q=None), 1), (dict(kc=None), 1), (dict(vc=None), 1), (dict(table=None), 1), (dict(lens=None), 1),
     (dict(out=None), 1), (dict(B=0), 1), (dict(H=0), 1), (dict(bs=0), 1), (dict(max_blocks=0), 1),
-    (dict(num_blocks=0), 1), (dict(scale=0.0), 1), (dict(scale=math.nan), 1), (dict(S=0), 1), (dict(S=1025), 1),
+    (dict(num_blocks=0), 1), (dict(scale=3e38), 1), (dict(scale=math.nan), 1), (dict(S=0), 1), (dict(S=1025), 1),
     (dict(dtype=0), 2), (dict(dtype=5), 2), (dict(d=96), 2),
     (dict(bs=12), 2), (dict(bs=2048), 2),
     (dict(max_blocks=1 << 27, bs=32), 2), (dict(num_blocks=1 << 29), 2),
@@ -290,7 +303,7 @@ def call_varlen(fa, ws_bytes=None, **over):
 
 @pytest.mark.parametrize("over,code", [
     (dict(q=None), 1), (dict(cq=None), 1), (dict(ck=None), 1), (dict(out=None), 1), (dict(S=0), 1),
-    (dict(total_q=0), 1), (dict(total_k=0), 1), (dict(H=0), 1), (dict(scale=-1.0), 1), (dict(causal=2), 1),
+    (dict(total_q=0), 1), (dict(total_k=0), 1), (dict(H=0), 1), (dict(scale=-math.inf), 1), (dict(causal=2), 1),
     (dict(dtype=0), 2), (dict(d=80), 2), (dict(S=4097), 2), (dict(total_q=1 << 25), 2),
     (dict(q=VQ + 8), 2), (dict(cq=VCQ + 2), 2), (dict(lse=VL + 1), 2),
     (dict(out=VK + 64), 1), (dict(lse=VCQ), 1), (dict(lse=VO + 16), 1),
@@ -339,7 +352,7 @@ def test_quantize_fp8_rejects_invalid_arguments(fa, over, code):
 
 
 @pytest.mark.parametrize("over,code", [
-    (dict(pack=None), 1), (dict(out=None), 1), (dict(H=0), 1), (dict(scale=0.0), 1), (dict(causal=5), 1),
+    (dict(pack=None), 1), (dict(out=None), 1), (dict(H=0), 1), (dict(scale=math.nan), 1), (dict(causal=5), 1),
     (dict(d=32), 2), (dict(dtype=0), 2), (dict(pack=FP + 64), 2), (dict(out=FO + 8), 2), (dict(lse=FL + 1), 2),
     (dict(out=FP + 1024), 1), (dict(lse=FO + 16), 1),
 ])

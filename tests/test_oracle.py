@@ -133,6 +133,31 @@ def test_oracle_matches_mpmath(causal, Nq, Nk, d, sigma):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("scale", [-0.35, -3.0, 0.0])
+def test_oracle_matches_mpmath_at_negative_and_zero_scale(causal, scale):
+    # the caller's scale may be any finite value ("08. Triton Flash
+    # Attention": the kernel takes sm_scale as an argument)
+    q, k, v = rand_qkv(1, 1, 6, 7, 5, seed=611, q_sigma=2.0)
+    out, lse = oracle.attention(q, k, v, scale, causal)
+    ref_o, ref_l = mp_attention(q[0, 0], k[0, 0], v[0, 0], scale, causal)
+    np.testing.assert_allclose(out[0, 0], ref_o, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse[0, 0], ref_l, rtol=1e-14, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_scale_gives_mean_of_visible_values(causal):
+    # every visible score is 0, so P is uniform over the visible keys:
+    # O_i = mean of the visible v_j and LSE_i = ln |J_i|
+    q, k, v = rand_qkv(1, 2, 20, 25, 8, seed=612, q_sigma=5.0)
+    out, lse = oracle.attention(q, k, v, 0.0, causal)
+    v64 = v.astype(np.float64)
+    for i in range(20):
+        n = (i + 1) if causal else 25
+        np.testing.assert_allclose(out[0, :, i], v64[0, :, :n].mean(axis=1), rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lse[0, :, i], math.log(n), rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("B,H,Nq,Nk,d", [(1, 1, 256, 256, 64), (2, 3, 100, 100, 64), (1, 2, 37, 61, 32),
                                          (1, 1, 70, 33, 128)])
 def test_oracle_matches_torch_fp64(causal, B, H, Nq, Nk, d):
