@@ -1,6 +1,6 @@
 """Benchmark of the FlashAttention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|all]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload configs|all|NAME]
 
 A step is one call of the forward (``fa_fwd``; ``fa_fwd_splitkv`` for the
 decode workload; ``fa_fwd_paged_decode`` for the paged-cache decode) over one
@@ -11,13 +11,20 @@ then K timed steps are bracketed by ``torch.cuda.synchronize()``.  Each step
 is also bracketed by events on the stream the kernels run on, which gives
 the per-launch kernel time used for the roofline fraction.
 
-The default workload is causal bf16 prefill, B=8, H=16, N=4096, d=128.
-FLOPs follow the convention 4*B*H*Nq*Nk*d (the two contractions), halved
-under the causal mask; bytes are one read of Q, K, V and one write of O and
-LSE.  One JSON line per workload goes to stdout.
+By default (``--workload configs``) the five configurations are timed in
+turn, one JSON line each: single-head fp32, ragged causal fp16, long
+non-causal bf16, single-token decode, and last the causal bf16 prefill
+B=8, H=16, N=4096, d=128, so that the final line is the headline.
+``--workload all`` adds the backward, FP8, paged-decode and variable-length
+workloads before the headline.  FLOPs follow the convention 4*B*H*Nq*Nk*d
+(the two contractions), halved under the causal mask; bytes are one read of
+Q, K, V and one write of O and LSE.
 
 The ``cpu_baseline`` leg times the fp64 oracle (test infrastructure) on a
-bounded sample of query rows of the same workload on the host cores.
+bounded sample of the same workload on the host cores, then compares the
+GPU output of the timed steps with the oracle on that sample (``check``:
+max and mean |dO|, max |dLSE|).  Each line also names the device and the
+ROCm version it ran on.
 """
 from __future__ import annotations
 
@@ -32,9 +39,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 DEFAULT_WORKLOAD = "prefill_causal_bf16_b8h16_n4096_d128"
+# the configurations, in the order they are timed: the headline last
+CONFIG_WORKLOADS = ["single_head_f32_n256_d64", "ragged_causal_f16_b2h8_n1000_d64",
+                    "long_bf16_b1h32_n16384_d128_qsigma8", "decode_bf16_b16h32_nk8192_d128_split32",
+                    DEFAULT_WORKLOAD]
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
-PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector (packed)
+# MI355X fp32 vector FMA without packed instructions (the library is built
+# with packed fp32 off): 256 CUs x 64 lanes x 2 FLOP x 2.4 GHz
+PEAK_FP32_TFLOPS = 78.6
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 # the sources each workload's dominant kernel is built from (a committed
 # traffic record is used only while their hash is unchanged)
@@ -104,9 +117,27 @@ def measured_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def bwd_cpu_baseline(w, q, k, v, target_s: float):
+def check_fields(o, l, ref_o, ref_l, what: str):
+    """max and mean |dO| and max |dLSE| of GPU outputs against the oracle's
+    on the rows the oracle computed (a row without keys must give O = 0 and
+    LSE = -inf on both sides; it counts in |dO| and must match in LSE)."""
+    import numpy as np
+    o = np.asarray(o, dtype=np.float64).reshape(ref_o.shape)
+    l = np.asarray(l, dtype=np.float64).reshape(ref_l.shape)
+    fin = np.isfinite(ref_l)
+    d_o = np.abs(o - ref_o)
+    rec = {"vs": "fp64 oracle", "rows": what, "max_abs_dO": float(d_o.max()), "mean_abs_dO": float(d_o.mean()),
+           "max_abs_dLSE": float(np.abs(l[fin] - ref_l[fin]).max()) if fin.any() else 0.0}
+    if not fin.all():
+        rec["rows_without_keys"] = int((~fin).sum())
+        rec["lse_neg_inf_match"] = bool(np.array_equal(np.isneginf(l), ~fin))
+    return rec
+
+
+def bwd_cpu_baseline(w, q, k, v, target_s: float, grads):
     """Time the fp64 backward oracle on whole heads (all query and key rows),
-    growing the number of heads until about ``target_s`` of work."""
+    growing the number of heads until about ``target_s`` of work; then
+    compare the GPU gradients of those heads with it."""
     import numpy as np
     import oracle
     import fa_inputs
@@ -115,43 +146,89 @@ def bwd_cpu_baseline(w, q, k, v, target_s: float):
     gf = fa_inputs.make_dout(w.B, w.H, w.Nq, w.d, w.dtype, w.seed).float().numpy()
     n = 1
     while True:
+        heads = np.arange(n)
         t0 = time.perf_counter()
-        oracle.attention_bwd(qf, kf, vf, gf, w.scale, w.causal, heads=np.arange(n), threads=threads)
+        ref = oracle.attention_bwd(qf, kf, vf, gf, w.scale, w.causal, heads=heads, threads=threads)
         dt = time.perf_counter() - t0
         if dt >= target_s or n >= w.B * w.H:
             break
         n = min(w.B * w.H, max(n + 1, int(n * target_s / max(dt, 1e-3) * 1.1)))
     flops = workload_flops(w) / (w.B * w.H) * n
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    base = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": "heads 0..%d of %d, all rows, %.1f s, fp64 backward oracle" % (n - 1, w.B * w.H, dt)}
+    check = {"vs": "fp64 backward oracle", "rows": "heads 0..%d, every row" % (n - 1)}
+    for name, g, r in zip(("dQ", "dK", "dV"), grads, ref):
+        x = g.float().cpu().numpy().astype(np.float64).reshape(w.B * w.H, -1, w.d)[:n]
+        r = np.asarray(r, dtype=np.float64).reshape(w.B * w.H, -1, w.d)[:n]
+        err = np.abs(x - r)
+        rms = float(np.sqrt((r ** 2).mean()))
+        check[name] = {"max_abs": float(err.max()), "max_rel_to_abs_plus_rms": float((err / (np.abs(r) + rms)).max()),
+                       "mean_abs_over_rms": float(err.mean() / rms) if rms > 0 else 0.0}
+    return base, check
 
 
-def cpu_baseline(w, q, k, v, target_s: float):
-    """Time the fp64 oracle on a sample of rows; returns the baseline object."""
+def cpu_baseline(w, q, k, v, target_s: float, out, lse):
+    """Time the fp64 oracle on a sample of rows; returns the baseline object
+    and the check of the GPU output (``out``, ``lse``) on those rows."""
     import numpy as np
     import oracle
-    import fa_inputs
-    if w.backward:
-        return bwd_cpu_baseline(w, q, k, v, target_s)
     threads = len(os.sched_getaffinity(0))
     qf, kf, vf = (t.float().numpy() for t in (q, k, v))   # exact widening, outside the timing
     total_rows = w.B * w.H * w.Nq
     n = min(total_rows, 256)
     elapsed, flops, rows_done = 0.0, 0.0, 0
+    reps = 1
     while True:
         rows = np.sort(np.random.default_rng(n).choice(total_rows, size=n, replace=False)).astype(np.int64)
         t0 = time.perf_counter()
-        oracle.attention(qf, kf, vf, w.scale, w.causal, rows=rows, threads=threads)
+        for _ in range(reps):
+            ref_o, ref_l = oracle.attention(qf, kf, vf, w.scale, w.causal, rows=rows, threads=threads)
         dt = time.perf_counter() - t0
         vis = oracle.visible_keys(w.Nq, w.Nk, w.causal, rows)
-        elapsed, flops, rows_done = dt, float(4.0 * w.d * vis.sum()), n
-        if dt >= target_s or n >= total_rows:
+        elapsed, flops, rows_done = dt, float(4.0 * w.d * vis.sum()) * reps, n
+        if dt >= target_s or (n >= total_rows and dt >= min(target_s, 1.0)):
             break
+        if n >= total_rows:  # a small workload: repeat the whole computation for a stable rate
+            reps = max(reps + 1, int(reps * min(target_s, 1.0) / max(dt, 1e-4) * 1.2))
         n = min(total_rows, max(n * 2, int(n * target_s / max(dt, 1e-3) * 1.1)))
     what = ("all %d query rows" % total_rows if rows_done == total_rows else
             "%d of %d query rows drawn uniformly (numpy seed %d)" % (rows_done, total_rows, rows_done))
-    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "%s, %.1f s, fp64 three-pass oracle" % (what, elapsed)}
+    base = {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%s%s, %.1f s, fp64 three-pass oracle"
+                      % (what, ", computed %d times" % reps if reps > 1 else "", elapsed)}
+    o = out.float().cpu().numpy().reshape(-1, w.d)[rows]
+    l = lse.cpu().numpy().reshape(-1)[rows]
+    return base, check_fields(o, l, ref_o, ref_l, what)
+
+
+def fp8_check(w, q, k, v, signs, out, lse, nrows=512):
+    """The FP8 output against exact attention on the dequantised inputs (the
+    FP8 oracle) on a sample of rows."""
+    import numpy as np
+    import fa_inputs
+    from oracle import fp8
+    rows = fa_inputs.sample_rows(w.B, w.H, w.Nq, nrows, seed=w.seed)
+    ro, rl, _ = fp8.fp8_attention(q, k, v, w.scale, w.causal, signs=signs.numpy(), rows=rows)
+    o = out.float().cpu().numpy().reshape(-1, w.d)[rows]
+    l = lse.cpu().numpy().reshape(-1)[rows]
+    rec = check_fields(o, l, ro.reshape(-1, w.d)[rows], rl.reshape(-1)[rows], "%d sampled query rows" % rows.size)
+    rec["vs"] = "fp64 attention on the dequantised E4M3 inputs"
+    return rec
+
+
+def environment():
+    """Device and software the line was measured on."""
+    import torch
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    props = torch.cuda.get_device_properties(0)
+    return {"device": "%s (%s, %d CUs)" % (props.name, getattr(props, "gcnArchName", "?"),
+                                            props.multi_processor_count),
+            "rocm": rocm, "torch_hip": torch.version.hip}
 
 
 def time_steps(step, steps, warmup, prewarm_s):
@@ -252,30 +329,39 @@ def run_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s=0.3):
         "roofline": roof,
     }
     rec.update(extra)
+    rec.update(environment())
     if with_cpu:
-        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, cpu_target_s)
+        if w.backward:
+            rec["cpu_baseline"], rec["check"] = bwd_cpu_baseline(w, q, k, v, cpu_target_s, (dq, dk, dv))
+        else:
+            rec["cpu_baseline"], rec["check"] = cpu_baseline(w, q, k, v, cpu_target_s, out, lse)
+            if w.fp8:
+                rec["check"] = fp8_check(w, q, k, v, signs.cpu(), out, lse)
     return rec
 
 
-def paged_cpu_baseline(w, q, kc, vc, table, lens, target_s: float):
+def paged_cpu_baseline(w, q, kc, vc, table, lens, target_s: float, out, lse):
     """Time the fp64 paged oracle (gather, then three-pass attention) on a
-    prefix of the sequences."""
+    prefix of the sequences; then check the GPU output of those sequences."""
     import oracle
     threads = len(os.sched_getaffinity(0))
     qf, kf, vf = (t.float() for t in (q, kc, vc))   # exact widening, outside the timing
     n = 1
     while True:
         t0 = time.perf_counter()
-        oracle.paged_decode(qf, kf, vf, table, lens, w.scale, seqs=range(n), threads=threads)
+        ref_o, ref_l = oracle.paged_decode(qf, kf, vf, table, lens, w.scale, seqs=range(n), threads=threads)
         dt = time.perf_counter() - t0
         if dt >= target_s or n >= w.B:
             break
         n = min(w.B, max(n + 1, int(n * target_s / max(dt, 1e-3) * 1.1)))
     keys = int(lens[:n].clamp(min=0).sum())
     flops = 4.0 * w.H * w.d * keys
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    base = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": "sequences 0..%d of %d (%d keys x %d heads), %.1f s, gather + fp64 three-pass oracle"
                       % (n - 1, w.B, keys, w.H, dt)}
+    o = out[:n, :, 0].float().cpu().numpy()
+    l = lse[:n].cpu().numpy()
+    return base, check_fields(o, l, ref_o, ref_l, "sequences 0..%d, every head" % (n - 1))
 
 
 def run_paged_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s):
@@ -315,8 +401,9 @@ def run_paged_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s):
                    "algorithmic_bytes_per_step": nbytes},
         "roofline": roof,
     }
+    rec.update(environment())
     if with_cpu:
-        rec["cpu_baseline"] = paged_cpu_baseline(w, q, kc, vc, table, lens, cpu_target_s)
+        rec["cpu_baseline"], rec["check"] = paged_cpu_baseline(w, q, kc, vc, table, lens, cpu_target_s, out, lse)
     return rec
 
 
@@ -367,6 +454,7 @@ def run_varlen_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s):
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(name)},
     }
+    rec.update(environment())
     if with_cpu:
         import oracle
         threads = len(os.sched_getaffinity(0))
@@ -374,18 +462,28 @@ def run_varlen_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s):
         order = list(np.argsort(lq))
         qf, kf, vf = (t.float() for t in (q, k, v))
         done, t_total, pairs = [], 0.0, 0
+        o_gpu, l_gpu = out.float().cpu().numpy(), lse.cpu().numpy()
+        got_o, got_l, want_o, want_l = [], [], [], []
         for sidx in order:
             t0 = time.perf_counter()
-            oracle.varlen_attention(qf, kf, vf, cq, ck, w.scale, w.causal, seqs=[int(sidx)], threads=threads)
+            ref_o, ref_l = oracle.varlen_attention(qf, kf, vf, cq, ck, w.scale, w.causal, seqs=[int(sidx)],
+                                                   threads=threads)
             t_total += time.perf_counter() - t0
             done.append(int(sidx))
             pairs += varlen_pairs(w, [lq[sidx]], [lk[sidx]])
+            r0, r1 = int(cq[sidx]), int(cq[sidx + 1])
+            got_o.append(o_gpu[r0:r1])
+            got_l.append(l_gpu[:, r0:r1].T)
+            want_o.append(ref_o[r0:r1])
+            want_l.append(ref_l[:, r0:r1].T)
             if t_total >= cpu_target_s:
                 break
         rec["cpu_baseline"] = {"value": 4.0 * w.d * w.H * pairs / t_total / 1e12, "unit": "TFLOP/s",
                                "cores": threads, "kind": "oracle",
                                "sample": "%d of %d sequences, shortest first (lengths %s), %.1f s, fp64 oracle"
                                          % (len(done), w.S, [lq[i] for i in done], t_total)}
+        rec["check"] = check_fields(np.concatenate(got_o), np.concatenate(got_l), np.concatenate(want_o),
+                                    np.concatenate(want_l), "sequences %s, every row and head" % done)
     return rec
 
 
@@ -410,9 +508,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--workload", default="configs",
+                    help="configs (the five configurations, headline last), all, or one workload name")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target oracle time for each line's cpu_baseline")
     ap.add_argument("--prewarm-s", type=float, default=0.3,
                     help="seconds of untimed steps before the warmup steps (lets the GPU clock ramp up)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -426,11 +526,17 @@ def main():
     if args.copy_bytes:
         return copy_probe(args.copy_bytes, args.steps)
     import fa_inputs
-    names = (list(fa_inputs.WORKLOADS) + list(fa_inputs.PAGED_WORKLOADS) + list(fa_inputs.VARLEN_WORKLOADS)
-             if args.workload == "all" else [args.workload])
-    for i, name in enumerate(names):
-        rec = run_workload(name, args.steps, args.warmup,
-                           with_cpu=(not args.no_cpu_baseline) and (i == 0 or args.workload != "all"),
+    if args.workload == "configs":
+        names = list(CONFIG_WORKLOADS)
+    elif args.workload == "all":
+        extra = [n for n in list(fa_inputs.WORKLOADS) + list(fa_inputs.PAGED_WORKLOADS) +
+                 list(fa_inputs.VARLEN_WORKLOADS) if n not in CONFIG_WORKLOADS]
+        names = CONFIG_WORKLOADS[:-1] + extra + [DEFAULT_WORKLOAD]
+    else:
+        names = [args.workload]
+    for name in names:
+        print("bench: %s" % name, file=sys.stderr, flush=True)
+        rec = run_workload(name, args.steps, args.warmup, with_cpu=not args.no_cpu_baseline,
                            cpu_target_s=args.cpu_seconds, prewarm_s=args.prewarm_s)
         print(json.dumps(rec), flush=True)
     return 0
