@@ -120,6 +120,33 @@ int fa_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
            int dtype, hipStream_t stream);
 
 /*
+ * fa_fwd_noalloc -- fa_fwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, checks and dispatch as fa_fwd, but the
+ * split workspace (decode, and prefill grids too small for the GPU) is a
+ * static device array of FA_NOALLOC_SCRATCH_BYTES bytes instead of the
+ * library cache, and the call allocates nothing.  Each GPU the library runs
+ * on holds its own copy of that array until the process ends; its address is
+ * looked up (hipGetSymbolAddress) on the first call on each device.
+ *
+ * Limit: a split whose workspace (B*H*Nq*chunks*(d + 1) float32) would not
+ * fit takes as many chunks as fit (the result then differs from fa_fwd's by
+ * rounding only); a prefill that fits fewer than two runs unsplit; a decode
+ * (Nq == 1, no mask) whose B*H*(d + 1)*4 bytes exceed the array is rejected
+ * with FA_ERR_WORKSPACE before any HIP call.  Where the workspace fits, the
+ * chunk count and the result are fa_fwd's, bit for bit.
+ *
+ * The array keeps the last call's contents; nothing in it needs clearing
+ * (every chunk slot is written before it is read).  All calls on one GPU
+ * share it: calls that overlap on one GPU (concurrent streams, or threads)
+ * race and must be serialised by the caller.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int fa_fwd_noalloc(const void *q, const void *k, const void *v, void *out,
+                   float *lse, int B, int H, int Nq, int Nk, int d,
+                   float scale, int causal, int dtype, hipStream_t stream);
+
+/*
  * fa_splitkv_workspace_bytes -- bytes of workspace fa_fwd_splitkv needs:
  * B*H*Nq*num_splits*(d + 1) float32 values (each chunk's normalised partial
  * output and its logsumexp), rounded up to 256 bytes.  Returns 0 for

@@ -27,6 +27,9 @@ _SIGNATURES = {
     "fa_fwd": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                               ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                               ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+    "fa_fwd_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "fa_splitkv_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 5),
     "fa_fwd_splitkv": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -157,6 +160,24 @@ def fa_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, return_lse=Tru
         scale = 1.0 / math.sqrt(d)
     _check(lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d, float(scale),
                       1 if causal else 0, _dtype_code(q), _stream_handle(q, stream)), "fa_fwd")
+    return out, lse
+
+
+# bytes of the static scratch array of fa_fwd_noalloc (FA_NOALLOC_SCRATCH_BYTES)
+FA_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def fa_fwd_noalloc(q, k, v, out, lse=None, scale=None, causal=False, stream=None):
+    """fa_fwd through the entry point that allocates no device memory (its
+    split workspace is the library's static scratch array).  ``out`` (and
+    ``lse``, if wanted) must be given.  Returns (out, lse)."""
+    B, H, Nq, Nk, d = _shapes(q, k, v)
+    if out is None:
+        raise ValueError("fa_fwd_noalloc writes into caller-owned outputs: pass out")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check(lib.fa_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d, float(scale),
+                              1 if causal else 0, _dtype_code(q), _stream_handle(q, stream)), "fa_fwd_noalloc")
     return out, lse
 
 

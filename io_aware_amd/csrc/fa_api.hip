@@ -145,20 +145,81 @@ int run_splitkv(const void *q, const void *k, const void *v, void *out, float *l
                       "split-KV launch");
 }
 
-}  // namespace
+// Where fa_fwd's split workspace comes from: the library's cache (hipMalloc
+// on first use per stream), or the static scratch array of fa_fwd_noalloc.
+enum class WsSource { kCache, kScratch };
 
-extern "C" {
+// Scratch of fa_fwd_noalloc: a file-scope device array, so the code object
+// loader places one copy on every GPU the library runs on, held until the
+// process ends.  In host code ``scratch`` names a host-side stand-in, not
+// device memory: host code uses only the address hipGetSymbolAddress gives
+// for the current device (kept per device below).  The split workspace
+// needs no clearing (every chunk slot is written before the combine reads
+// it), and calls that overlap on one GPU share the array and race.
+constexpr size_t kScratchBytes = FA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) char scratch[kScratchBytes];
 
-int fa_fwd(const void *q, const void *k, const void *v, void *out, float *lse, int B, int H, int Nq, int Nk, int d,
-           float scale, int causal, int dtype, hipStream_t stream) {
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];  // device address of each device's copy, or null before first use
+
+int get_scratch(size_t need, void **out) {
+    if (need > kScratchBytes)  // also checked by the caller before any HIP call
+        return fail(FA_ERR_WORKSPACE, "fa_fwd_noalloc: the call needs " + std::to_string(need) +
+                                          " bytes of scratch, more than its " + std::to_string(kScratchBytes));
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return hip_status(err, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(FA_ERR_HIP, "fa_fwd_noalloc: device index out of range");
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {  // first call on this device (it is current): find its copy
+        void *p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return hip_status(err != hipSuccess ? err : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return FA_OK;
+}
+
+// The largest chunk count whose split workspace (B*H*Nq rows of S*(d + 1)
+// float32) fits in the scratch array.
+int scratch_max_splits(int B, int H, int Nq, int d) {
+    const size_t per_split = (size_t)B * H * Nq * ((size_t)d + 1) * sizeof(float);
+    const size_t s = kScratchBytes / per_split;
+    return s > (size_t)kMaxSplits ? kMaxSplits : (int)s;
+}
+
+// fa_fwd and fa_fwd_noalloc: checks, then dispatch (see fa.h).  With the
+// scratch source a split that would not fit the scratch array takes fewer
+// chunks (as many as fit); a prefill then runs unsplit if fewer than two
+// fit, and a decode that cannot fit one chunk is rejected before any HIP
+// call.
+int forward(const void *q, const void *k, const void *v, void *out, float *lse, int B, int H, int Nq, int Nk,
+            int d, float scale, int causal, int dtype, hipStream_t stream, WsSource src) {
     int st = check_common(q, k, v, out, lse, B, H, Nq, Nk, d, scale, dtype);
     if (st != FA_OK) return st;
     if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+    const bool scratch_src = src == WsSource::kScratch;
+    auto take = [&](size_t need, void **ws) {
+        return scratch_src ? get_scratch(need, ws) : get_workspace(need, stream, ws);
+    };
 
     if (Nq == 1 && !causal && dtype != FA_F32) {
-        const int S = fa_default_num_splits(Nk);
+        int S = fa_default_num_splits(Nk);
+        if (scratch_src) {
+            const int fit = scratch_max_splits(B, H, 1, d);
+            if (fit < 1)
+                return fail(FA_ERR_WORKSPACE, "fa_fwd_noalloc: B*H*(d + 1)*4 = " +
+                                                  std::to_string(workspace_bytes(B, H, 1, d, 1)) +
+                                                  " bytes exceed its scratch of " + std::to_string(kScratchBytes));
+            S = S < fit ? S : fit;
+        }
         void *ws = nullptr;
-        st = get_workspace(workspace_bytes(B, H, 1, d, S), stream, &ws);
+        st = take(workspace_bytes(B, H, 1, d, S), &ws);
         if (st != FA_OK) return st;
         return run_splitkv(q, k, v, out, lse, B, H, Nk, d, scale, S, ws, dtype, stream);
     }
@@ -167,10 +228,14 @@ int fa_fwd(const void *q, const void *k, const void *v, void *out, float *lse, i
         return hip_status(fa::launch_prefill_f32(d, causal == 1, q, k, v, out, lse, B * H, Nq, Nk, sl, stream),
                           "fp32 prefill launch");
     const int shape = prefill_shape(d);
-    const int S = fa::prefill_split_count(d, causal == 1, shape, B * H, Nq, Nk);
+    int S = fa::prefill_split_count(d, causal == 1, shape, B * H, Nq, Nk);
+    if (S > 1 && scratch_src) {
+        const int fit = scratch_max_splits(B, H, Nq, d);
+        if (fit < S) S = fit >= 2 ? fa::prefill_split_normalise(d, causal == 1, shape, Nq, Nk, fit) : 1;
+    }
     if (S > 1) {  // a grid too small for the GPU: split the key range, then combine
         void *ws = nullptr;
-        st = get_workspace(workspace_bytes(B, H, Nq, d, S), stream, &ws);
+        st = take(workspace_bytes(B, H, Nq, d, S), &ws);
         if (st != FA_OK) return st;
         return hip_status(fa::launch_prefill_split(dtype, d, causal == 1, shape, q, k, v, out, lse, B * H, Nq, Nk,
                                                    sl, S, ws, stream),
@@ -178,6 +243,20 @@ int fa_fwd(const void *q, const void *k, const void *v, void *out, float *lse, i
     }
     return hip_status(fa::launch_prefill(dtype, d, causal == 1, shape, q, k, v, out, lse, B * H, Nq, Nk, sl, stream),
                       "prefill launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void *q, const void *k, const void *v, void *out, float *lse, int B, int H, int Nq, int Nk, int d,
+           float scale, int causal, int dtype, hipStream_t stream) {
+    return forward(q, k, v, out, lse, B, H, Nq, Nk, d, scale, causal, dtype, stream, WsSource::kCache);
+}
+
+int fa_fwd_noalloc(const void *q, const void *k, const void *v, void *out, float *lse, int B, int H, int Nq, int Nk,
+                   int d, float scale, int causal, int dtype, hipStream_t stream) {
+    return forward(q, k, v, out, lse, B, H, Nq, Nk, d, scale, causal, dtype, stream, WsSource::kScratch);
 }
 
 size_t fa_splitkv_workspace_bytes(int B, int H, int Nq, int d, int num_splits) {

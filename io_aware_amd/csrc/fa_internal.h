@@ -72,6 +72,9 @@ hipError_t launch_prefill_varlen(int dtype, int d, bool causal, int shape, const
 // merges them into out and lse.  prefill_split_count chooses S (1: no split;
 // FA_PREFILL_SPLIT = 0 disables, a number n >= 2 asks for n chunks).
 int prefill_split_count(int d, bool causal, int shape, int BH, int Nq, int Nk);
+// At most S chunks of whole tiles, none of them empty: the count a split
+// launch of the shape runs with (1: no split).
+int prefill_split_normalise(int d, bool causal, int shape, int Nq, int Nk, int S);
 hipError_t launch_prefill_split(int dtype, int d, bool causal, int shape, const void *q, const void *k,
                                 const void *v, void *out, float *lse, int BH, int Nq, int Nk, float scale_log2,
                                 int S, void *workspace, hipStream_t stream);

@@ -745,6 +745,12 @@ int prefill_split_count(int d, bool causal, int shape, int BH, int Nq, int Nk) {
         S = S < by_len ? S : by_len;
         S = S < 64 ? S : 64;
     }
+    return prefill_split_normalise(d, causal, shape, Nq, Nk, S);
+}
+
+int prefill_split_normalise(int d, bool causal, int shape, int Nq, int Nk, int S) {
+    const int key_tiles = split_key_tiles(shape, d, causal, Nq, Nk);
+    S = S < key_tiles ? S : key_tiles;
     if (S < 2) return 1;
     // whole tiles per chunk; drop chunks that would start past the keys
     const int chunk_tiles = (key_tiles + S - 1) / S;

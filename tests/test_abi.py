@@ -39,7 +39,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for want in ("fa_fwd", "fa_fwd_fp8", "fa_quantize_fp8", "fa_fp8_pack_bytes", "fa_fwd_varlen", "fa_varlen_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_paged_decode", "fa_splitkv_workspace_bytes", "fa_status_string",
+    for want in ("fa_fwd", "fa_fwd_noalloc", "fa_fwd_fp8", "fa_quantize_fp8", "fa_fp8_pack_bytes", "fa_fwd_varlen", "fa_varlen_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_paged_decode", "fa_splitkv_workspace_bytes", "fa_status_string",
                  "fa_last_error", "fa_release_workspace", "fa_default_num_splits", "fa_map_workgroup"):
         assert want in names
 
@@ -98,12 +98,39 @@ def test_every_finite_scale_passes_validation(fa, scale):
     # the scale check runs before the head-dim check: an accepted scale
     # leaves the call to be rejected for d = 48 (unsupported), not for scale
     assert call_fwd(fa, scale=scale, d=48) == 2
+    assert call_fwd_noalloc(fa, scale=scale, d=48) == 2
     assert "d must be" in fa.fa_last_error()
     assert call_split(fa, scale=scale, d=48) == 2
     assert call_paged(fa, scale=scale, d=48) == 2
     assert call_bwd(fa, scale=scale, d=48) == 2
     assert call_varlen(fa, scale=scale, d=48) == 2
     assert call_fwd_fp8(fa, scale=scale, dtype=0) == 2   # its size checks come first: reject the out type
+
+
+def call_fwd_noalloc(fa, **over):
+    a = dict(GOOD)
+    a.update(over)
+    return fa.lib.fa_fwd_noalloc(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"], a["Nq"], a["Nk"],
+                                 a["d"], a["scale"], a["causal"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), 1), (dict(B=0), 1), (dict(scale=math.nan), 1), (dict(causal=2), 1), (dict(dtype=3), 2),
+    (dict(d=48), 2), (dict(out=O + 4), 2), (dict(out=Q + 64), 1),
+    # a decode whose one-chunk workspace, B*H*(d + 1)*4 bytes, exceeds the scratch array
+    (dict(B=1024, H=64, Nq=1, Nk=1, d=128), 4),
+])
+def test_fwd_noalloc_rejects_invalid_arguments(fa, over, code):
+    assert call_fwd_noalloc(fa, **over) == code
+    assert fa.fa_last_error() != ""
+
+
+def test_noalloc_scratch_size_is_the_header_constant(fa):
+    text = open(HEADER).read()
+    m = re.search(r"#define FA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == fa.FA_NOALLOC_SCRATCH_BYTES
+    # the decode workload (16 x 32 heads, d = 128, 32 chunks) fits it
+    assert fa.fa_splitkv_workspace_bytes(16, 32, 1, 128, 32) <= fa.FA_NOALLOC_SCRATCH_BYTES
 
 
 def test_error_message_is_per_thread(fa):
