@@ -264,8 +264,9 @@ size_t fa_fp8_pack_bytes(int B, int H, int Nq, int Nk, int d);
 /*
  * fa_quantize_fp8 -- q [B, H, Nq, d], k and v [B, H, Nk, d] (dtype fp16 or
  * bf16) -> pack.  signs: device float [d] of +-1 (the random diagonal of
- * M = H_d diag(signs) / sqrt(d), H_d the Sylvester-Hadamard matrix), or NULL
- * for no transform (M = I).  The transform is the fast Walsh-Hadamard
+ * M = diag(signs) H_d / sqrt(d), applied to each row x as x M: the signs
+ * first, then H_d, the Sylvester-Hadamard matrix), or NULL for no
+ * transform (M = I).  The transform is the fast Walsh-Hadamard
  * butterfly in float32.  pack: at least fa_fp8_pack_bytes bytes, 256-byte
  * aligned, not overlapping the inputs.
  */

@@ -3,7 +3,8 @@
 // Method ("9.4 FlashAttention 与 FlashMLA" section 9.4.4, the FP8 mode of
 // FlashAttention-3): Q, K and V enter the matrix products as 8-bit floats;
 // before quantisation Q and K are multiplied by one random orthogonal matrix
-// M = H_d diag(s) / sqrt(d) (the same for both, so Q K^T is unchanged), which
+// M = diag(s) H_d / sqrt(d) (rows x -> x M: signs, then the Hadamard
+// butterfly; the same M for both, so Q K^T is unchanged), which
 // spreads large-magnitude channels over all channels and evens out the
 // quantisation error.  V is quantised as it is.
 //

@@ -8,8 +8,9 @@ the quantisation error of Q and K spread evenly by a random orthogonal
 transform applied to both ("incoherent processing").  The page fixes neither
 the transform nor the scaling; the readings taken here:
 
-* the transform is M = H_d diag(s) / sqrt(d): the signs s (random, +-1, drawn
-  by the caller and passed in) then the Sylvester-Hadamard matrix H_d.  The
+* the transform is M = diag(s) H_d / sqrt(d), each row x going to x M: the
+  signs s (random, +-1, drawn by the caller and passed in) first, then the
+  Sylvester-Hadamard matrix H_d.  The
   same M goes to Q and K, so (Q M)(K M)^T = Q K^T and the scores are
   unchanged before rounding.  V is not transformed;
 * one scale per (batch, head) and tensor: amax = max |x| over the head,
