@@ -316,3 +316,20 @@ def sample_rows(B: int, H: int, Nq: int, count: int, seed: int, tile: int = 64):
     while len(picked) < min(count, total):
         picked.add(int(rng.integers(0, total)))
     return np.array(sorted(picked), dtype=np.int64)
+
+
+def make_rising_scores(N: int, d: int, seed: int = 77, value_exp: int = 94):
+    """q [1, 1, 64, d], k and v [1, 1, N, d] in bf16 that stress the lazy
+    rescale's range: every query is [1, 0, ...]; key j's first dim is
+    j * 29 / (c (N - 1)) with c = scale * log2(e) at scale 1/sqrt(d) (so the
+    scaled scores climb by 29 in base 2 over the sequence), its other dims
+    N(0, 0.01^2); values uniform in [1, 1.1) * 2^value_exp.  Drawn from a CPU
+    generator seeded with ``seed`` (k's noise, then v)."""
+    g = torch.Generator().manual_seed(int(seed))
+    c = float(np.float32(default_scale(d) * 1.4426950408889634))
+    q = torch.zeros(64, d)
+    q[:, 0] = 1.0
+    k = torch.randn(N, d, generator=g) * 0.01
+    k[:, 0] = torch.arange(N) * (29.0 / (c * (N - 1)))
+    v = (1.0 + 0.1 * torch.rand(N, d, generator=g)) * 2.0 ** value_exp
+    return tuple(t.to(torch.bfloat16)[None, None] for t in (q, k, v))

@@ -22,6 +22,10 @@
  * probabilities (a convex combination of value rows) while LSE comes from
  * the float32 sum, and O is rounded to the input type (nearest-even).
  * (The single-token split-KV path keeps its probabilities in float32.)
+ * Range: probabilities are formed against a row max that may lag the
+ * exact one; the lag is bounded so that with bf16 inputs O stays finite for
+ * |V| up to 2^96 (about 7.9e28) whatever the key count, and with fp16
+ * inputs for every finite V.
  *
  * Causal mask (``causal`` = 1): key j is visible to query i iff j <= i
  * (top-left alignment, for any Nq and Nk; "6. FlashAttention 分块逻辑",

@@ -38,10 +38,11 @@
 //    co-resident waves of a SIMD in different phases.
 //  * Lazy rescale: P is formed against the max the row is held at; the
 //    accumulator is rescaled (and the held max moved to the exact running
-//    max) only when some lane's tile sum of P exceeds 2^15 (fp16, largest
-//    finite 65504) or 2^30 (bf16).  Until then every P stays within that
-//    bound, which the 16-bit type and float32 hold without loss of relative
-//    precision, and no per-tile row max is needed;
+//    max) only when some lane's sum of P exceeds the bound: 2^15 over the
+//    tile for fp16 (largest finite 65504), 2^30 since the last exact step
+//    for bf16 (which also bounds the accumulator).  Until then every P stays
+//    within that bound, which the 16-bit type and float32 hold without loss
+//    of relative precision, and no per-tile row max is needed;
 //    O and LSE are the same function of the inputs because acc, l and m
 //    always refer to the same held max.  (With scores of large spread the
 //    running max keeps growing; at 2^8 the exact step ran more often: the
@@ -100,12 +101,17 @@ constexpr int kModeDense = 0;
 constexpr int kModeVarlen = 1;
 constexpr int kModeSplit = 2;
 
-// Bound on a lane's per-tile sum of P between rescales; it keeps every
-// P <= bound (see the online-softmax step of prefill_kernel): P rounded to
-// fp16 must stay below 65504; bf16 has float32's exponent range, and 2^30
-// keeps the float32 sums and the accumulator far from overflow.
+// Bound of the lazy rescale (see the online-softmax step of prefill_kernel).
+// fp16: on a lane's sum of P over one tile, which keeps every P within
+// 2^15, so P rounded to fp16 stays below its largest finite 65504.  bf16 has
+// float32's exponent range, so the bound is on the lane's running sum of P
+// since the last exact step: every P, the row sums and the accumulator
+// (|acc| <= 2 * 2^30 * max|V| over the two lane halves) stay finite for
+// |V| up to 2^96, whatever the length of the key range.
 template <typename T>
 constexpr float held_sum_bound() { return __is_same(T, _Float16) ? 32768.0f : 0x1p30f; }
+template <typename T>
+constexpr bool running_sum_bound() { return !__is_same(T, _Float16); }
 constexpr float kLn2 = 0.693147180559945309417f;
 
 template <typename T, int D, bool CAUSAL, int NW, int QW, int BC, int OCC, int MODE>
@@ -348,9 +354,9 @@ void prefill_kernel(PrefillArgs a) {
 
         // ---- online softmax -------------------------------------------------
         // P = exp2(c*s - m_held) and its row sums are formed first.  A lane's
-        // tile sum <= the bound bounds each of its P by it (P >= 0), which is the
-        // lazy-rescale invariant, so the row max is only needed when some lane
-        // of the wave exceeds it (or has no held max yet).  Then the exact
+        // tile sum (bf16: running sum) <= the bound bounds each of its P by it
+        // (P >= 0), which is the lazy-rescale invariant, so the row max is only
+        // needed when some lane of the wave exceeds it (or has no held max yet).  Then the exact
         // step runs on the untouched scores: m_new = max(m_held, rowmax),
         // rescale acc and l by exp2(m_held - m_new), recompute P.
         x8 pf[QB][KS2];
@@ -378,7 +384,8 @@ void prefill_kernel(PrefillArgs a) {
             bool exact = __ballot(m_held[qb] == -__builtin_inff()) != 0ull;
             if (!exact) {
                 lsum = exp_tile(m_held[qb]);
-                exact = __ballot(!(lsum <= held_sum_bound<T>())) != 0ull;  // also true for inf / NaN
+                const float held = running_sum_bound<T>() ? l_part[qb] + lsum : lsum;
+                exact = __ballot(!(held <= held_sum_bound<T>())) != 0ull;  // also true for inf / NaN
             }
             if (exact) {
                 float mx = -__builtin_inff();

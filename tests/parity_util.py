@@ -13,6 +13,19 @@ TOL = {"f32": (1e-5, None), "f16": (2e-2, 2e-3), "bf16": (2e-2, 2e-3)}
 LSE_TOL = 1e-3
 DEV = "cuda:0"
 
+# Bars with no stated tolerance on the pages, each about twice the largest
+# figure of a CPU model of the kernels' rounding points on the cases the
+# GPU tests run (tests/rounding_models.py; recomputed by tests/test_models.py,
+# which asserts that every bar covers its model):
+# * backward, per gradient tensor: (max |x - ref| / (|ref| + rms(ref)),
+#   mean |x - ref| / rms(ref)) for bf16 and fp16;
+# * FP8 forward against exact attention on the dequantised inputs: max and
+#   mean |dO|, max |dLSE|; and mean |dO| against exact attention on the
+#   original inputs (quantisation included).
+BWD_TOL = {"bf16": (0.125, 6e-3), "f16": (0.016, 1e-3)}
+FP8_MAX, FP8_MEAN, FP8_LSE = 0.12, 8e-3, 1e-3
+FP8_EXACT_MEAN = 1e-2
+
 
 def note(msg):
     print(msg, flush=True)

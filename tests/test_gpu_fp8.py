@@ -8,15 +8,16 @@ C ABI.
 * Forward (``fa_fwd_fp8``) against exact attention on the same dequantised
   inputs.  The kernel rounds P to E4M3 before P V' (3 mantissa bits) and
   normalises by the sum of the rounded P; the pages give no bound for FP8,
-  so the bar comes from the arithmetic: a CPU model of those rounding points
-  (P relative to a held max up to 2^8 above it, rounded to E4M3; the sum of
-  the rounded P; float32 accumulation; bf16 output) against the oracle gives
-  at most max |dO| = 0.11 and mean |dO| = 5.2e-3 over causal and non-causal
-  cases, d = 64 and 128, N up to 4096 and q scaled by 8.  The tests allow
-  about twice that:
-      max |dO| <= 0.2,  mean |dO| <= 1e-2,  max |dLSE| <= 1e-3.
+  so the bar comes from the arithmetic: tests/rounding_models.py models
+  those rounding points on the CPU (P relative to a held max up to 2^8
+  above it, rounded to E4M3; the sum of the rounded P; float32
+  accumulation; bf16 output), and on the cases below (the same shapes and
+  seeds) gives at most max |dO| = 0.070 and mean |dO| = 3.8e-3, matching
+  what the GPU measures (tests/test_models.py recomputes them).  The tests
+  allow about 1.7x and 2x that (parity_util):
+      max |dO| <= 0.12,  mean |dO| <= 8e-3,  max |dLSE| <= 1e-3.
 * End to end against exact attention on the unquantised inputs (q not
-  scaled): the model gives mean |dO| <= 3.4e-3 + 1.7e-3; the test allows
+  scaled): the model gives mean |dO| of at most 5e-3; the test allows
   mean |dO| <= 1e-2.
 """
 import numpy as np
@@ -26,11 +27,9 @@ import torch
 import fa_inputs
 import oracle
 from oracle import fp8
-from parity_util import DEV, note, to_dev
+from parity_util import DEV, FP8_EXACT_MEAN, FP8_LSE, FP8_MAX, FP8_MEAN, note, to_dev
 
 pytestmark = pytest.mark.gpu
-
-FP8_MAX, FP8_MEAN, FP8_LSE = 0.2, 1e-2, 1e-3
 
 
 @pytest.fixture(scope="module")
@@ -134,7 +133,7 @@ def run_fp8(fa, B, H, Nq, Nk, d, causal, seed, q_sigma=1.0, transform=True, exac
         eo, _ = oracle.attention(q, k, v, scale, causal)
         e2 = np.abs(o - eo)
         note("%s vs exact: max|dO|=%.3e mean|dO|=%.3e" % (label, e2.max(), e2.mean()))
-        assert e2.mean() <= 1e-2, label
+        assert e2.mean() <= FP8_EXACT_MEAN, label
     return out, lse
 
 

@@ -16,9 +16,8 @@ import torch
 import fa_inputs
 import oracle
 from oracle import fp8
-from parity_util import DEV, LSE_TOL, compare, note, to_dev
+from parity_util import DEV, FP8_LSE, FP8_MAX, FP8_MEAN, LSE_TOL, compare, note, to_dev
 from test_gpu_backward import compare_grad
-from test_gpu_fp8 import FP8_LSE, FP8_MAX, FP8_MEAN
 from test_gpu_paged import run_paged
 
 pytestmark = pytest.mark.gpu
