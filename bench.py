@@ -159,7 +159,7 @@ def bwd_cpu_baseline(w, q, k, v, target_s: float, grads):
     check = {"vs": "fp64 backward oracle", "rows": "heads 0..%d, every row" % (n - 1)}
     for name, g, r in zip(("dQ", "dK", "dV"), grads, ref):
         x = g.float().cpu().numpy().astype(np.float64).reshape(w.B * w.H, -1, w.d)[:n]
-        r = np.asarray(r, dtype=np.float64).reshape(w.B * w.H, -1, w.d)[:n]
+        r = np.asarray(r, dtype=np.float64)   # [n, N, d]: the heads computed
         err = np.abs(x - r)
         rms = float(np.sqrt((r ** 2).mean()))
         check[name] = {"max_abs": float(err.max()), "max_rel_to_abs_plus_rms": float((err / (np.abs(r) + rms)).max()),
