@@ -337,18 +337,24 @@ void prefill_kernel(PrefillArgs a) {
         __builtin_amdgcn_s_setprio(0);
 
         // ---- mask: ragged key tail and the causal diagonal ------------------
+        // Register r of 32-key block kb holds key base + acc_row(r, 0) with
+        // base = k0 + 32 kb + 4 g (acc_row(r, g) = acc_row(r, 0) + 4 g), so
+        // one per-lane limit, the last visible offset, decides all 16: a
+        // compare with the constant acc_row(r, 0) and a select each.
         const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > q0w);
         if (need_mask) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
                 const int qrow = q0w + 32 * qb + l32;
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
+                for (int kb = 0; kb < KB; ++kb) {
+                    const int base = k0 + 32 * kb + 4 * g;
+                    int lim = Nk - 1 - base;
+                    if constexpr (CAUSAL) lim = min(lim, qrow - base);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + 32 * kb + layout::acc_row(r, g);
-                        if (key >= Nk || (CAUSAL && key > qrow)) s[qb][kb][r] = -__builtin_inff();
-                    }
+                    for (int r = 0; r < 16; ++r)
+                        if (layout::acc_row(r, 0) > lim) s[qb][kb][r] = -__builtin_inff();
+                }
             }
         }
 
@@ -397,14 +403,19 @@ void prefill_kernel(PrefillArgs a) {
                 const float m_new = __builtin_fmaxf(m_held[qb], mx * c);  // c > 0 (the sign is in Q)
                 const float alpha =
                     (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_held[qb] - m_new);
+                // a wave whose rows have no held max yet (its first block) has
+                // nothing accumulated: no rescale
+                const bool held_any = __ballot(m_held[qb] != -__builtin_inff()) != 0ull;
                 m_held[qb] = m_new;
-                l_part[qb] *= alpha;
-                // lane n < 16 keeps queries n (register 0) and n + 16 (register 1)
-                const float alpha_hi = __shfl(alpha, (lane + 16) & 63);
-                lt[qb][0] *= alpha;
-                lt[qb][1] *= alpha_hi;
+                if (held_any) {
+                    l_part[qb] *= alpha;
+                    // lane n < 16 keeps queries n (register 0) and n + 16 (register 1)
+                    const float alpha_hi = __shfl(alpha, (lane + 16) & 63);
+                    lt[qb][0] *= alpha;
+                    lt[qb][1] *= alpha_hi;
 #pragma unroll
-                for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha;
+                    for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha;
+                }
                 // a row that has seen no key yet keeps m = -inf: subtract 0
                 // there so masked scores give exp2(-inf) = 0, not NaN
                 lsum = exp_tile((m_new == -__builtin_inff()) ? 0.0f : m_new);
