@@ -107,17 +107,24 @@ typedef enum fa_status {
  * path ("6. FlashAttention 分块逻辑", section 11: K/V split into chunks that
  * are processed independently, then merged by logsumexp weights) with
  * fa_default_num_splits(Nk) chunks and a library-owned workspace kept per
- * (device, stream); any other shape runs the tiled prefill kernel.  A
- * 16-bit prefill whose grid of (batch*head, Q block) workgroups is too small
- * to give every CU two of them (fewer than 512), and whose Q blocks read
- * enough K/V tiles (the causal mask counted: 32 for grids of at most 128
- * workgroups, 256 above), has the key range of each Q block cut into
- * min(ceil(512 / grid), tiles / 8, 64) chunks of whole K/V tiles as well
- * (fewer where whole-tile chunks need fewer), one workgroup each, and
- * the chunks merged by the same logsumexp combine, through the same
- * library-owned workspace (B*H*Nq*chunks*(d + 1) float32).  The environment
- * variable FA_PREFILL_SPLIT overrides the choice: 0 or 1 never splits, n >= 2
- * asks for n chunks (capped at the tile count).
+ * (device, stream); any other shape runs the tiled prefill kernel.  Grids of
+ * (batch*head, Q block of 128) workgroups too small for the GPU are split
+ * along the keys, by the same method at two levels:
+ *  - fewer than 512 workgroups whose Q blocks read many K/V tiles (the
+ *    causal mask counted: 64 for grids of at most 128 workgroups, 256
+ *    above), for 16-bit types: the key range of each Q block is cut into
+ *    min(ceil(512 / grid), tiles / 8, 64) chunks of whole tiles (fewer where
+ *    whole-tile chunks need fewer), one workgroup each, merged by the same
+ *    logsumexp combine through the same library-owned workspace
+ *    (B*H*Nq*chunks*(d + 1) float32);
+ *  - otherwise, fewer than 256 workgroups whose longest Q block reads at
+ *    least 8 tiles: Q blocks of 32 (64 at d = 128 or above 128 workgroups)
+ *    queries whose key tiles are shared out between 4 (2) waves of the
+ *    workgroup, their partial results merged the same way in shared
+ *    memory, with no workspace.
+ * The environment variable FA_PREFILL_SPLIT overrides the first choice: 0
+ * or 1 never splits, n >= 2 asks for n chunks (capped at the tile count);
+ * FA_PREFILL_SHAPE forces a tile shape (sweeps).
  */
 int fa_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
            int B, int H, int Nq, int Nk, int d, float scale, int causal,

@@ -88,12 +88,23 @@ size_t workspace_bytes(int B, int H, int Nq, int d, int S) {
     return (floats * sizeof(float) + 255) / 256 * 256;
 }
 
-// Prefill tile shape: FA_PREFILL_SHAPE (0 .. 3) for sweeps, else the
-// measured best for the head dim -- 32-key tiles at three waves per SIMD for
-// d = 128, 64-key tiles at two waves per SIMD below.
-int prefill_shape(int d) {
+// Prefill tile shape forced by FA_PREFILL_SHAPE (0 .. kNumPrefillShapes - 1,
+// for sweeps), or -1.
+int env_shape() {
     const char *env = std::getenv("FA_PREFILL_SHAPE");
     if (env && env[0] >= '0' && env[0] < '0' + fa::kNumPrefillShapes && env[1] == '\0') return env[0] - '0';
+    return -1;
+}
+
+bool key_split_shape(int shape) { return shape == fa::kShapeW4Q32K2 || shape == fa::kShapeW4Q32K4; }
+
+// The shape of full-grid, split and variable-length launches: the forced
+// one unless it is a key-split shape, else the measured best for the head
+// dim -- 32-key tiles at three waves per SIMD for d = 128, 64-key tiles at
+// two waves per SIMD below.
+int prefill_shape(int d) {
+    const int e = env_shape();
+    if (e >= 0 && !key_split_shape(e)) return e;
     return d >= 128 ? fa::kShapeW4Q32B32 : fa::kShapeW4Q32;
 }
 
@@ -227,7 +238,7 @@ int forward(const void *q, const void *k, const void *v, void *out, float *lse, 
     if (dtype == FA_F32)
         return hip_status(fa::launch_prefill_f32(d, causal == 1, q, k, v, out, lse, B * H, Nq, Nk, sl, stream),
                           "fp32 prefill launch");
-    const int shape = prefill_shape(d);
+    int shape = prefill_shape(d);
     int S = fa::prefill_split_count(d, causal == 1, shape, B * H, Nq, Nk);
     if (S > 1 && scratch_src) {
         const int fit = scratch_max_splits(B, H, Nq, d);
@@ -241,6 +252,8 @@ int forward(const void *q, const void *k, const void *v, void *out, float *lse, 
                                                    sl, S, ws, stream),
                           "split prefill launch");
     }
+    // a grid below one workgroup per CU: the key loop split over the waves of a workgroup
+    shape = env_shape() >= 0 ? env_shape() : fa::prefill_small_grid_shape(d, causal == 1, shape, B * H, Nq, Nk);
     return hip_status(fa::launch_prefill(dtype, d, causal == 1, shape, q, k, v, out, lse, B * H, Nq, Nk, sl, stream),
                       "prefill launch");
 }

@@ -40,11 +40,20 @@ enum PrefillShape {
     kShapeW4Q64 = 1,   // 4 waves x 64 queries = Br 256, Bc 64
     kShapeW2Q64 = 2,   // 2 waves x 64 queries = Br 128, Bc 64
     kShapeW4Q32B32 = 3,  // 4 waves x 32 queries = Br 128, Bc 32, three waves per SIMD
-    kNumPrefillShapes = 4
+    kShapeW4Q32K2 = 4,   // 4 waves, 2 query groups of 32, each group's K/V tiles split over 2 waves
+                         // (Br 64; Bc 64, d = 128: 32)
+    kShapeW4Q32K4 = 5,   // 4 waves on one group of 32 queries, its tiles split over 4 waves
+                         // (Br 32; Bc 32, d = 32: 64; d = 128 takes kShapeW4Q32K2)
+    kNumPrefillShapes = 6
 };
 
 // Queries per workgroup (Br) of a prefill shape.
 int prefill_block_rows(int shape);
+
+// The shape a dense launch takes when the grid of ``shape`` would leave
+// CUs idle and each Q block's key loop is long: a key-split shape, else
+// ``shape``.
+int prefill_small_grid_shape(int d, bool causal, int shape, int BH, int Nq, int Nk);
 
 // bf16 / fp16 tiled forward (MFMA).  dtype is FA_F16 or FA_BF16; d in
 // {32, 64, 128}.  scale_log2 = scale * log2(e).

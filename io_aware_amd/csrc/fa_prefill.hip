@@ -114,7 +114,7 @@ template <typename T>
 constexpr bool running_sum_bound() { return !__is_same(T, _Float16); }
 constexpr float kLn2 = 0.693147180559945309417f;
 
-template <typename T, int D, bool CAUSAL, int NW, int QW, int BC, int OCC, int MODE>
+template <typename T, int D, bool CAUSAL, int NW, int QW, int BC, int OCC, int MODE, int KSPLIT = 1>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC)))
 void prefill_kernel(PrefillArgs a) {
     constexpr bool VARLEN = MODE == kModeVarlen;
@@ -122,8 +122,12 @@ void prefill_kernel(PrefillArgs a) {
     using M = Mfma<T>;
     using x8 = typename M::x8;
     using x4 = typename M::x4;
+    // KSPLIT > 1 (grids too small for the GPU): KSPLIT waves share one group
+    // of QW queries and take turns over its K/V tiles (wave part p takes
+    // tiles p, p + KSPLIT, ...); each step stages KSPLIT consecutive tiles,
+    // and at the end the parts' (m, l, acc) are merged through LDS.
     constexpr int NT = NW * 64;      // threads per workgroup
-    constexpr int BR = NW * QW;      // query rows per workgroup
+    constexpr int BR = NW / KSPLIT * QW;  // query rows per workgroup
     constexpr int QB = QW / 32;      // 32-query column blocks per wave
     constexpr int KS = D / 16;       // k-steps of S^T = K Q^T
     constexpr int DB = D / 32;       // 32-dim row blocks of O^T
@@ -131,11 +135,13 @@ void prefill_kernel(PrefillArgs a) {
     constexpr int KS2 = BC / 16;     // k-steps of O^T = V^T P^T
     constexpr int CH = D / 8;        // 16-byte chunks per row of K or V
     constexpr int ROW = D * 2;       // bytes per key row
-    constexpr int TILE_BYTES = BC * ROW;
-    constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K tile + V tile
-    constexpr int UNITS = BC * CH;               // 16-byte units per tile
-    constexpr int NDMA = UNITS / NT;             // DMA instructions per thread per tile (each of K, V)
+    constexpr int BCS = KSPLIT * BC;             // keys staged per step
+    constexpr int TILE_BYTES = BCS * ROW;        // the K (or V) rows of one step
+    constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K rows + V rows
+    constexpr int UNITS = BCS * CH;              // 16-byte units per step
+    constexpr int NDMA = UNITS / NT;             // DMA instructions per thread per step (each of K, V)
     static_assert(QW % 32 == 0 && BC % 32 == 0 && D % 32 == 0, "tile shape");
+    static_assert(NW % KSPLIT == 0 && (KSPLIT == 1 || MODE == kModeDense), "key split: dense launches only");
     static_assert(UNITS % NT == 0, "a tile must split evenly over the workgroup");
     static_assert(2 * STAGE_BYTES <= 65536, "stage offsets must fit a 16-bit LDS immediate");
 
@@ -189,8 +195,9 @@ void prefill_kernel(PrefillArgs a) {
         lsep = a.lse ? a.lse + (size_t)bh * Nq : nullptr;
     }
     const int RSB = RS * 2;  // bytes between rows
+    const int kpart = KSPLIT > 1 ? wave % KSPLIT : 0;  // the wave's share of the key tiles
     const int q0 = qblk * BR;
-    const int q0w = q0 + wave * QW;
+    const int q0w = q0 + wave / KSPLIT * QW;
     const float c = a.scale_log2;
     const uint32_t kv_bytes = Nk > 0 ? (uint32_t)(Nk - 1) * RSB + ROW : 0u;
     const __amdgpu_buffer_rsrc_t rsrc_k = __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(kp), (short)0, (int)kv_bytes, kBufferDword3);
@@ -209,15 +216,15 @@ void prefill_kernel(PrefillArgs a) {
     // per-lane operand read offsets (bytes within a tile, block / k-step 0)
     int koff[KS], voff[DB];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) koff[ks] = layout::k_operand_offset<D>(0, l32, g, ks);
+    for (int ks = 0; ks < KS; ++ks) koff[ks] = layout::k_operand_offset<D>(0, l32, g, ks) + kpart * BC * ROW;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) voff[db] = layout::v_operand_tr_offset<D>(db, lane, 0, 0);
+    for (int db = 0; db < DB; ++db) voff[db] = layout::v_operand_tr_offset<D>(db, lane, 0, 0) + kpart * BC * ROW;
 
     auto issue_tile = [&](int k0, int stage) {
         char *kbase = smem + stage * STAGE_BYTES;
         char *vbase = kbase + TILE_BYTES;
         const uint32_t soff = (uint32_t)k0 * RSB;
-        const bool tail = k0 + BC > Nk;  // workgroup-uniform
+        const bool tail = k0 + BCS > Nk;  // workgroup-uniform
 #pragma unroll
         for (int n = 0; n < NDMA; ++n) {
             uint32_t ko = kdma[n], vo = vdma[n];
@@ -287,7 +294,7 @@ void prefill_kernel(PrefillArgs a) {
     // keys [kbeg, kend) of this workgroup: all visible ones, or one chunk
     const int kbeg = SPLIT ? min(kv_end, chunk_idx * a.chunk) : 0;
     const int kend = SPLIT ? min(kv_end, kbeg + a.chunk) : kv_end;
-    const int nt = (kend - kbeg + BC - 1) / BC;
+    const int nt = (kend - kbeg + BCS - 1) / BCS;  // steps
 
     auto compute_tile = [&](auto stage_tag, int k0) {
         constexpr int S = decltype(stage_tag)::value;
@@ -463,10 +470,12 @@ void prefill_kernel(PrefillArgs a) {
 
     auto step = [&](auto stage_tag, int jt) {
         constexpr int S = decltype(stage_tag)::value;
-        const int k0 = kbeg + jt * BC;
-        if (jt + 1 < nt) issue_tile(k0 + BC, S ^ 1);
-        // wave-uniform: the wave has live queries that see some key of this block
-        const bool active = (q0w < Nq) && (!CAUSAL || k0 <= q0w + QW - 1);
+        const int ks0 = kbeg + jt * BCS;
+        if (jt + 1 < nt) issue_tile(ks0 + BCS, S ^ 1);
+        const int k0 = ks0 + kpart * BC;
+        // wave-uniform: the wave has live queries that see some key of its block
+        const bool active =
+            (q0w < Nq) && (KSPLIT == 1 || k0 < kend) && (!CAUSAL || k0 <= q0w + QW - 1);
         if (active) compute_tile(stage_tag, k0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's DMA of block jt+1 has landed
         __syncthreads();                                    // ... and every thread's; stage S is free
@@ -482,9 +491,70 @@ void prefill_kernel(PrefillArgs a) {
         if (jt + 1 < nt) step(Int<1>{}, jt + 1);
     }
 
+    // ---- key split: merge the parts of each query group --------------------
+    // Parts 1 .. KSPLIT-1 write (m, l, lt, acc) to LDS (free after the last
+    // step's barrier, field-major so that lanes hit consecutive banks); part 0
+    // merges them as the split-KV combine does: M = max(m, m'), each side
+    // weighed by exp2(m - M) (0 for a side without keys).
+    if constexpr (KSPLIT > 1) {
+        constexpr int NF = QB * (DB * 16 + 6);  // floats per lane per part
+        static_assert((NW / KSPLIT) * (KSPLIT - 1) * NF * 64 * 4 <= 2 * STAGE_BYTES, "merge buffer");
+        float *mbuf = reinterpret_cast<float *>(smem);
+        const int base = (wave / KSPLIT) * (KSPLIT - 1) * NF;
+        if (kpart > 0) {
+            float *dst = mbuf + (base + (kpart - 1) * NF) * 64 + lane;
+            int f = 0;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                dst[64 * f++] = m_held[qb];
+                dst[64 * f++] = l_part[qb];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dst[64 * f++] = lt[qb][r];
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) dst[64 * f++] = oacc[qb][db][r];
+            }
+        }
+        __syncthreads();
+        if (kpart == 0) {
+#pragma unroll
+            for (int part = 1; part < KSPLIT; ++part) {
+                const float *src = mbuf + (base + (part - 1) * NF) * 64 + lane;
+                int f = 0;
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    const float m2 = src[64 * f++];
+                    const float l2 = src[64 * f++];
+                    const float mm = __builtin_fmaxf(m_held[qb], m2);
+                    const bool none = mm == -__builtin_inff();
+                    const float a1 = none ? 0.0f : __builtin_amdgcn_exp2f(m_held[qb] - mm);
+                    const float a2 = none ? 0.0f : __builtin_amdgcn_exp2f(m2 - mm);
+                    m_held[qb] = mm;
+                    l_part[qb] = __builtin_fmaf(l2, a2, l_part[qb] * a1);
+                    // lane n < 16 keeps the rounded sums of queries n (register
+                    // 0) and n + 16 (register 1)
+                    const float a1_hi = __shfl(a1, (lane + 16) & 63), a2_hi = __shfl(a2, (lane + 16) & 63);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float lt2 = src[64 * f++];
+                        lt[qb][r] = r == 1 ? __builtin_fmaf(lt2, a2_hi, lt[qb][r] * a1_hi)
+                                           : __builtin_fmaf(lt2, a2, lt[qb][r] * a1);
+                    }
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            oacc[qb][db][r] = __builtin_fmaf(src[64 * f++], a2, oacc[qb][db][r] * a1);
+                }
+            }
+        }
+    }
+
     // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2 --------------------
     // (split launch: this chunk's normalised partial o~ = acc / l and its
     // logsumexp, -inf with o~ = 0 where the chunk holds no visible key)
+    if (kpart != 0) return;  // wave-uniform: the merged state is in part 0
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const float l = xor32_sum(l_part[qb]);
@@ -637,10 +707,19 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(const in
     if (tid == 0) sched[0] = T < max_tiles ? T : max_tiles;  // only decreasing offsets can exceed the bound
 }
 
-template <typename T, int D, bool CAUSAL, int NW, int QW, int OCC, int BC = 64>
+template <typename T, int D, bool CAUSAL, int NW, int QW, int OCC, int BC = 64, int KSPLIT = 1>
 hipError_t launch_one(const PrefillArgs &base, bool varlen, int S, hipStream_t stream) {
-    constexpr int BR = NW * QW;
+    constexpr int BR = NW / KSPLIT * QW;
     PrefillArgs a = base;
+    if constexpr (KSPLIT > 1) {  // dense launches only (the host never asks otherwise)
+        if (varlen || a.S > 1) return hipErrorInvalidValue;
+        a.Tr = (a.Nq + BR - 1) / BR;
+        const long long nwg = (long long)a.BH * a.Tr;
+        if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((prefill_kernel<T, D, CAUSAL, NW, QW, BC, OCC, kModeDense, KSPLIT>), dim3((unsigned)nwg),
+                           dim3(NW * 64), 0, stream, a);
+        return hipGetLastError();
+    }
     if (!varlen) {
         a.Tr = (a.Nq + BR - 1) / BR;
         const long long nwg = (long long)a.BH * a.Tr;
@@ -678,6 +757,14 @@ hipError_t launch_shape(int shape, const PrefillArgs &a, bool varlen, int S, hip
         case kShapeW4Q32B32:  // a 32-key tile of d = 32 is too small to split over 256 threads
             if constexpr (D >= 64) return launch_one<T, D, CAUSAL, 4, 32, 3, 32>(a, varlen, S, stream);
             else return launch_one<T, D, CAUSAL, 4, 32, 2>(a, varlen, S, stream);
+        // key splits: two steps of staged keys must fit 64 KB of LDS
+        case kShapeW4Q32K2:
+            if constexpr (D >= 128) return launch_one<T, D, CAUSAL, 4, 32, 3, 32, 2>(a, varlen, S, stream);
+            else return launch_one<T, D, CAUSAL, 4, 32, 2, 64, 2>(a, varlen, S, stream);
+        case kShapeW4Q32K4:
+            if constexpr (D >= 128) return launch_one<T, D, CAUSAL, 4, 32, 3, 32, 2>(a, varlen, S, stream);
+            else if constexpr (D == 64) return launch_one<T, D, CAUSAL, 4, 32, 2, 32, 4>(a, varlen, S, stream);
+            else return launch_one<T, D, CAUSAL, 4, 32, 2, 64, 4>(a, varlen, S, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -714,14 +801,33 @@ hipError_t launch_any(int dtype, int d, bool causal, int shape, const PrefillArg
 
 }  // namespace
 
+static int prefill_block_cols(int shape, int d);
+
 int prefill_block_rows(int shape) {
     switch (shape) {
         case kShapeW4Q32: return 128;
         case kShapeW4Q64: return 256;
         case kShapeW2Q64: return 128;
         case kShapeW4Q32B32: return 128;
+        case kShapeW4Q32K2: return 64;
+        case kShapeW4Q32K4: return 32;  // 64 at d = 128, which takes the two-way split
         default: return 0;
     }
+}
+
+int prefill_small_grid_shape(int d, bool causal, int shape, int BH, int Nq, int Nk) {
+    // Below one workgroup per CU the time is the key loop of the longest Q
+    // block, one tile after another in each wave; splitting that loop over
+    // KSPLIT waves of the workgroup shortens it KSPLIT-fold for one merge
+    // through LDS.  Worth it once the loop holds enough tiles.
+    const int br = prefill_block_rows(shape);
+    if (br <= 0 || BH < 1 || Nq < 1 || Nk < 1) return shape;
+    const long long grid = (long long)BH * ((Nq + br - 1) / br);
+    const long long rows = (long long)(Nq + br - 1) / br * br;
+    const long long keys = causal && rows < Nk ? rows : Nk;  // the longest Q block's key range
+    const int bc = prefill_block_cols(shape, d);
+    if (grid >= 256 || keys < 8LL * bc) return shape;
+    return (grid <= 128 && d <= 64) ? kShapeW4Q32K4 : kShapeW4Q32K2;
 }
 
 // Keys per K/V tile of a shape at head dim d (shape 3 falls back to shape 0
@@ -752,11 +858,13 @@ int prefill_split_count(int d, bool causal, int shape, int BH, int Nq, int Nk) {
     } else {
         // Split only when the grid cannot give every CU two workgroups and
         // the key loop is long enough to pay for the fixed cost of a chunk
-        // and of the combine launch (about 6 us together): 32 tiles while
-        // at most half the CUs have a workgroup, 256 tiles beyond that,
+        // and of the combine launch (about 6 us together): 64 tiles while
+        // at most half the CUs have a workgroup (below that the key loop is
+        // split over the waves of each workgroup instead, which needs no
+        // second launch: prefill_small_grid_shape), 256 tiles beyond that,
         // where the chunks must share CUs.  Keep at least 8 tiles per chunk.
         constexpr long long kTargetGrid = 512;
-        const int min_tiles = grid <= 128 ? 32 : 256;
+        const int min_tiles = grid <= 128 ? 64 : 256;
         if (grid >= kTargetGrid || key_tiles < min_tiles) return 1;
         S = (int)((kTargetGrid + grid - 1) / grid);
         const int by_len = key_tiles / 8;

@@ -135,7 +135,7 @@ def test_ragged_shapes(fa, dtype, d, causal, split, monkeypatch):
                  label="B%d H%d Nq%d Nk%d d%d %s causal=%d split=%s" % (B, H, Nq, Nk, d, dtype, causal, split))
 
 
-@pytest.mark.parametrize("shape_id", [0, 1, 2, 3])
+@pytest.mark.parametrize("shape_id", [0, 1, 2, 3, 4, 5])
 @pytest.mark.parametrize("split", ["0", "3"])
 def test_every_prefill_tile_shape(fa, shape_id, split, monkeypatch):
     monkeypatch.setenv("FA_PREFILL_SHAPE", str(shape_id))
@@ -163,13 +163,13 @@ def test_split_prefill_chunk_counts(fa, split, monkeypatch):
 @pytest.mark.parametrize("B,H,Nq,Nk,d,dtype,causal,chunks", [
     (1, 2, 300, 5000, 64, "bf16", False, 9),     # grid 6, 79 tiles of 64 keys: 9 chunks of 9 tiles
     (1, 1, 2500, 6000, 128, "bf16", True, 10),   # grid 20; the mask leaves 2560 keys = 80 tiles of 32
-    (1, 4, 500, 2100, 32, "f16", False, 4),      # grid 16, 33 tiles: 4 chunks of 9 tiles
+    (1, 4, 500, 2100, 32, "f16", False, 1),      # grid 16, 33 tiles: under 64, the waves split the keys instead
     (2, 4, 1000, 1000, 64, "f16", True, 1),      # 16 tiles per Q block: too short to split
     (3, 48, 128, 2048, 32, "f16", False, 1),     # grid 144 with 32 tiles: chunks would share CUs
 ])
 def test_split_prefill_automatic_choice(fa, B, H, Nq, Nk, d, dtype, causal, chunks, monkeypatch):
     """Without FA_PREFILL_SPLIT, a grid under 512 workgroups whose Q blocks
-    read at least 32 K/V tiles (256 above 128 workgroups) is split into
+    read at least 64 K/V tiles (256 above 128 workgroups) is split into
     min(ceil(512 / grid), tiles / 8, 64) chunks (then as many as whole-tile
     chunks need): parity with the oracle, and bitwise the result of asking
     for that chunk count."""
@@ -184,7 +184,32 @@ def test_split_prefill_automatic_choice(fa, B, H, Nq, Nk, d, dtype, causal, chun
     assert torch.equal(auto[0], forced[0]) and torch.equal(auto[1], forced[1])
 
 
-@pytest.mark.parametrize("shape_id", [0, 3])
+@pytest.mark.parametrize("B,H,Nq,Nk,d,dtype,causal,shape", [
+    (2, 8, 1000, 1000, 64, "f16", True, 5),       # the ragged workload: grid 128, 16 tiles: four-way key split
+    (1, 4, 700, 900, 32, "bf16", False, 5),       # d = 32: four-way with 64-key tiles
+    (2, 8, 1000, 1000, 128, "bf16", True, 4),     # d = 128: two-way
+    (1, 40, 600, 1500, 64, "bf16", False, 4),     # grid 200, between 128 and 256: two-way
+    (4, 16, 1000, 1000, 64, "f16", True, None),   # grid 512: no key split
+    (2, 8, 300, 300, 64, "f16", True, None),      # 5 tiles per Q block: no key split
+])
+def test_key_split_automatic_choice(fa, B, H, Nq, Nk, d, dtype, causal, shape, monkeypatch):
+    """A dense grid below one workgroup per CU whose longest Q block reads
+    at least 8 K/V tiles splits each query group's key loop over 2 or 4
+    waves of the workgroup (merged through LDS): parity with the oracle, and
+    bitwise the result of forcing that shape (or the default one)."""
+    monkeypatch.delenv("FA_PREFILL_SPLIT", raising=False)
+    monkeypatch.delenv("FA_PREFILL_SHAPE", raising=False)
+    q, k, v, _, _ = run_full(fa, B, H, Nq, Nk, d, dtype, causal, seed=780 + d, q_sigma=3.0,
+                             label="auto key split B%d H%d Nq%d Nk%d d%d %s causal=%d" % (B, H, Nq, Nk, d, dtype, causal))
+    qd, kd, vd = to_dev(q, k, v)
+    auto = fa.fa_fwd(qd, kd, vd, causal=causal)
+    monkeypatch.setenv("FA_PREFILL_SHAPE", str(shape if shape is not None else (3 if d == 128 else 0)))
+    forced = fa.fa_fwd(qd, kd, vd, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(auto[0], forced[0]) and torch.equal(auto[1], forced[1])
+
+
+@pytest.mark.parametrize("shape_id", [0, 3, 4, 5])
 def test_prefill_shape_edge_cases(fa, shape_id, monkeypatch):
     """Key counts below, at and above the query count, single keys and
     queries, partial blocks of queries and keys, at d = 128 for the 64-key

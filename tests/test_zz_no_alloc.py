@@ -60,9 +60,11 @@ def test_decode_full_size_then_smaller(fa):
 
 
 def test_split_prefill_then_smaller(fa):
-    # grids of 2 and 3 workgroups over long key ranges: the key range is split
-    check_pair(fa, [(1, 2, 128, 8192, 128), (1, 3, 100, 2500, 64)], False, "bf16", 3110, "split prefill")
-    check_pair(fa, [(1, 2, 1000, 4000, 128), (1, 1, 700, 700, 128)], True, "f16", 3120, "split causal")
+    # grids of 2 to 20 workgroups over key ranges of 64 tiles or more: the
+    # key range is split into chunks merged through the scratch (the last
+    # case's 22 tiles are split over the waves of each workgroup instead)
+    check_pair(fa, [(1, 2, 128, 8192, 128), (1, 3, 100, 5000, 64)], False, "bf16", 3110, "split prefill")
+    check_pair(fa, [(1, 1, 2500, 4000, 128), (1, 1, 700, 700, 128)], True, "f16", 3120, "split causal")
 
 
 def test_prefill_and_f32_need_no_scratch(fa):
