@@ -89,6 +89,35 @@ __device__ __forceinline__ float hi_to_f32<_Float16>(uint32_t w) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
+// x plus the value of lane (lane of the same 16-lane row) by a DPP move:
+// CTRL is the data-parallel-primitive control of the move.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+    return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF,
+                                                                      false));
+}
+
+// Sum over the N lanes of a key row (N = 4, 8 or 16 consecutive lanes inside
+// one 16-lane DPP row), every lane receiving the total: VALU moves within
+// the row instead of LDS-crossbar exchanges.  N = 16: rotate by 8, then by 4
+// (each lane then holds the sum of its residue class mod 4), then the quad
+// exchanges 2 and 1.  N = 8: the half-row mirror pairs lane i with 7 - i,
+// leaving each quad with the four pair sums, then the quad exchanges.
+template <int N>
+__device__ __forceinline__ float row_sum(float x) {
+    constexpr int kRor8 = 0x128, kRor4 = 0x124, kHalfMirror = 0x141;
+    constexpr int kQuadXor2 = 0x4E, kQuadXor1 = 0xB1;  // quad_perm [2,3,0,1], [1,0,3,2]
+    static_assert(N == 4 || N == 8 || N == 16, "a key row spans 4, 8 or 16 lanes");
+    if constexpr (N == 16) {
+        x = dpp_add<kRor8>(x);
+        x = dpp_add<kRor4>(x);
+    } else if constexpr (N == 8) {
+        x = dpp_add<kHalfMirror>(x);
+    }
+    x = dpp_add<kQuadXor2>(x);
+    return dpp_add<kQuadXor1>(x);
+}
+
 // Stage one.  PAGED selects where key j of (b, h) lives: contiguous K/V at
 // row (b*H + h)*Nk + j, or, for a paged cache ("6. FlashAttention 分块逻辑"
 // section 12), at row (blk*H + h)*block_size + j % block_size of physical
@@ -179,8 +208,7 @@ __global__ __launch_bounds__(kSplitThreads) void splitkv_partial_kernel(SplitArg
                 dot = __builtin_fmaf(qv[2 * w], lo_to_f32<T>(kx[i][w]), dot);
                 dot = __builtin_fmaf(qv[2 * w + 1], hi_to_f32<T>(kx[i][w]), dot);
             }
-#pragma unroll
-            for (int msk = CH / 2; msk > 0; msk >>= 1) dot += __shfl_xor(dot, msk);
+            dot = row_sum<CH>(dot);
             s[i] = (roff[i] >= 0) ? dot * c : -__builtin_inff();
             mx = __builtin_fmaxf(mx, s[i]);
         }
