@@ -503,6 +503,153 @@ def copy_probe(nbytes: int, steps: int) -> int:
     return 0
 
 
+# The rocprofv3 passes --summarize-rocprof reads, one directory each under
+# DIR, with the command that fills it (run from the repository root).
+PROFILE_PASSES = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d {dir}/trace -o trace -- "
+             "python -u bench.py --workload {w} --steps 10 --warmup 2 --no-cpu-baseline",
+    "sq": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS "
+          "SQ_ACTIVE_INST_VALU SQ_WAVE_CYCLES GRBM_GUI_ACTIVE --output-format csv -d {dir}/sq -o sq -- "
+          "python -u bench.py --workload {w} --steps 2 --warmup 1 --prewarm-s 0 --no-cpu-baseline",
+    "lds": "rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY "
+           "GRBM_GUI_ACTIVE --output-format csv -d {dir}/lds -o lds -- "
+           "python -u bench.py --workload {w} --steps 2 --warmup 1 --prewarm-s 0 --no-cpu-baseline",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {dir}/fetch -o fetch -- "
+             "python -u bench.py --workload {w} --steps 2 --warmup 1 --prewarm-s 0 --no-cpu-baseline",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {dir}/write -o write -- "
+             "python -u bench.py --workload {w} --steps 2 --warmup 1 --prewarm-s 0 --no-cpu-baseline",
+    "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {dir}/copy_fetch -o copy_fetch -- "
+                  "python -u bench.py --copy-bytes 1073741824 --steps 3",
+    "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {dir}/copy_write -o copy_write -- "
+                  "python -u bench.py --copy-bytes 1073741824 --steps 3",
+}
+COPY_BYTES = 1073741824
+
+
+def _find_csv(root: str, suffix: str):
+    import glob
+    hits = sorted(glob.glob(os.path.join(root, "**", "*" + suffix), recursive=True))
+    return hits[-1] if hits else None
+
+
+def _counters(path: str, pattern: str, largest: bool = False):
+    """{counter: mean value per dispatch} and the mean dispatch duration (us)
+    of the kernels whose name contains ``pattern``, from a rocprofv3
+    counter_collection.csv; with ``largest``, each counter's largest
+    per-dispatch value instead of the mean (the copy probe's own dispatches,
+    not the fill that creates its source)."""
+    import csv
+    per = {}
+    durs = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if pattern not in row.get("Kernel_Name", ""):
+                continue
+            disp = row.get("Dispatch_Id") or row.get("Correlation_Id")
+            name = row["Counter_Name"]
+            per.setdefault(name, {}).setdefault(disp, 0.0)
+            per[name][disp] += float(row["Counter_Value"])
+            try:
+                durs[disp] = (float(row["End_Timestamp"]) - float(row["Start_Timestamp"])) / 1e3
+            except (KeyError, ValueError):
+                pass
+    means = {n: (max(v.values()) if largest else sum(v.values()) / len(v)) for n, v in per.items() if v}
+    dur = sum(durs.values()) / len(durs) if durs else None
+    return means, dur
+
+
+def summarize_rocprof(root: str, workload: str, out_dir: str, kernel: str = None) -> int:
+    """Write profiles/<kernel>_<workload>.md and profiles/traffic_<workload>.json
+    from the rocprofv3 passes under ``root`` (see PROFILE_PASSES).  ``kernel``
+    names another kernel of the run than the workload's dominant one (its
+    summary is written, the traffic record is not)."""
+    import csv
+    family, pattern = workload_kernel(workload)
+    dominant = kernel is None or kernel == pattern
+    pattern = kernel or pattern
+    lines = ["# rocprofv3 summary: `%s` kernel, workload %s" % (pattern, workload), ""]
+    trace = _find_csv(os.path.join(root, "trace"), "kernel_stats.csv")
+    avg_us = None
+    if trace:
+        lines += ["Kernel trace (`--kernel-trace --stats`), every kernel of the run:", "",
+                  "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+        with open(trace) as f:
+            for row in csv.DictReader(f):
+                name = row["Name"]
+                avg = float(row["AverageNs"]) / 1e3
+                lines.append("| `%s` | %s | %.1f | %.1f | %.1f |" % (name, row["Calls"], avg, float(row["MinNs"]) / 1e3,
+                                                                 float(row["MaxNs"]) / 1e3))
+                if pattern in name and (avg_us is None or avg > avg_us):
+                    avg_us = avg
+        lines.append("")
+    c = {}
+    dur = None
+    for pas in ("sq", "lds", "fetch", "write"):
+        path = _find_csv(os.path.join(root, pas), "counter_collection.csv")
+        if path:
+            m, d = _counters(path, pattern)
+            c.update(m)
+            dur = dur or d
+    if c:
+        lines += ["Counters of `%s` (`--pmc`, one pass per group, averaged over its dispatches):" % pattern, ""]
+        grbm = c.get("GRBM_GUI_ACTIVE")
+        per_xcd = grbm / 8.0 if grbm else None
+        if per_xcd and dur:
+            lines.append("- GRBM_GUI_ACTIVE per XCD: %.0f cycles over a %.0f us dispatch -> %.2f GHz effective clock"
+                         % (per_xcd, dur, per_xcd / dur / 1e3))
+        if per_xcd and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+            lines.append("- MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs)): %.1f %%"
+                         % (100.0 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (per_xcd * 1024)))
+        if "SQ_INSTS_MFMA" in c and "SQ_INSTS_VALU" in c:
+            lines.append("- SQ_INSTS_MFMA %.4g, SQ_INSTS_VALU %.4g (VALU/MFMA = %.2f), SQ_INSTS_LDS %.4g"
+                         % (c["SQ_INSTS_MFMA"], c["SQ_INSTS_VALU"], c["SQ_INSTS_VALU"] / max(c["SQ_INSTS_MFMA"], 1),
+                            c.get("SQ_INSTS_LDS", float("nan"))))
+        for a, b in (("SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES"), ("SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY")):
+            if a in c and b in c:
+                lines.append("- %s %.4g vs %s %.4g" % (a, c[a], b, c[b]))
+        if "SQ_LDS_BANK_CONFLICT" in c and "SQ_LDS_IDX_ACTIVE" in c:
+            lines.append("- SQ_LDS_BANK_CONFLICT %.0f of SQ_LDS_IDX_ACTIVE %.4g cycles (%.2f %%)"
+                         % (c["SQ_LDS_BANK_CONFLICT"], c["SQ_LDS_IDX_ACTIVE"],
+                            100.0 * c["SQ_LDS_BANK_CONFLICT"] / max(c["SQ_LDS_IDX_ACTIVE"], 1)))
+    traffic = None
+    cf, _ = _counters(_find_csv(os.path.join(root, "copy_fetch"), "counter_collection.csv") or os.devnull, "", True)
+    cw, _ = _counters(_find_csv(os.path.join(root, "copy_write"), "counter_collection.csv") or os.devnull, "", True)
+    if "FETCH_SIZE" in c and "WRITE_SIZE" in c and cf.get("FETCH_SIZE") and cw.get("WRITE_SIZE"):
+        # the copy reads and writes COPY_BYTES once: scale each counter to that
+        fs = COPY_BYTES / 1024.0 / cf["FETCH_SIZE"]
+        ws = COPY_BYTES / 1024.0 / cw["WRITE_SIZE"]
+        traffic = (c["FETCH_SIZE"] * fs + c["WRITE_SIZE"] * ws) * 1024.0
+        import fa_inputs
+        alg = None
+        if workload in fa_inputs.WORKLOADS:
+            alg = workload_bytes(fa_inputs.WORKLOADS[workload])
+        lines.append("- FETCH_SIZE %.0f KiB, WRITE_SIZE %.0f KiB per dispatch; copy calibration (1 GiB copy) "
+                     "reads back FETCH x%.4f, WRITE x%.4f" % (c["FETCH_SIZE"], c["WRITE_SIZE"], fs, ws))
+        lines.append("- HBM traffic per launch of `%s` (calibrated): %.4f GB%s" % (
+            pattern, traffic / 1e9, "" if alg is None else "; algorithmic bytes of the whole step %.4f GB (ratio %.2f)"
+            % (alg / 1e9, traffic / alg)))
+    lines += ["", "Commands (each run from the repository root; OUT is a scratch directory), then "
+              "`python bench.py --summarize-rocprof OUT --workload %s`:" % workload, ""]
+    for pas in PROFILE_PASSES:
+        if os.path.isdir(os.path.join(root, pas)):
+            lines.append("    " + PROFILE_PASSES[pas].format(dir="OUT", w=workload))
+    os.makedirs(out_dir, exist_ok=True)
+    md = "%s_%s.md" % (pattern, workload)
+    with open(os.path.join(out_dir, md), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    if traffic is not None and dominant:
+        rec = {"workload": workload, "kernel": pattern, "kernel_source_hash": kernel_source_hash(family),
+               "fetch_kib_per_dispatch": c["FETCH_SIZE"], "write_kib_per_dispatch": c["WRITE_SIZE"],
+               "copy_fetch_scale": fs, "copy_write_scale": ws, "hbm_bytes_per_launch": traffic,
+               "kernel_avg_us_under_profiler": avg_us, "summary": md}
+        with open(os.path.join(out_dir, "traffic_%s.json" % workload), "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+    print("\n".join(lines))
+    return 0
+
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -518,7 +665,22 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of attention, run --steps plain device-to-device copies of this many bytes "
                          "(the reference kernel for calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--summarize-rocprof", metavar="DIR", default=None,
+                    help="write profiles/<kernel>_<workload>.md and profiles/traffic_<workload>.json from the "
+                         "rocprofv3 passes under DIR (one subdirectory per pass, see PROFILE_PASSES); no GPU")
+    ap.add_argument("--kernel", default=None,
+                    help="with --summarize-rocprof: summarise the kernel whose name contains this instead of the "
+                         "workload's dominant one")
+    ap.add_argument("--print-profile-commands", metavar="DIR", default=None,
+                    help="print the rocprofv3 commands whose output --summarize-rocprof DIR reads")
     args = ap.parse_args()
+    if args.summarize_rocprof:
+        return summarize_rocprof(args.summarize_rocprof, args.workload, os.path.join(ROOT, "profiles"),
+                                 kernel=args.kernel)
+    if args.print_profile_commands:
+        for cmd in PROFILE_PASSES.values():
+            print(cmd.format(dir=args.print_profile_commands, w=args.workload))
+        return 0
     if args.gpus != 1:
         print("bench.py: this forward runs on one GPU; --gpus %d is not supported (use --gpus 1)" % args.gpus,
               file=sys.stderr)
