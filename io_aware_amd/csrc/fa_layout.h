@@ -187,8 +187,10 @@ FA_HD int tr_src_elem(int i) { return i & 3; }
 //    keys.  (Two heads at a time in one phase left the long blocks of the
 //    last pairs to the end: 5.5% slower on causal B8 H16 N4096.)
 //  * Otherwise (and when nwg is a multiple of 8, XCD x receives the work
-//    range [x*nwg/8, (x+1)*nwg/8)): heads two at a time, alternating between
-//    the pair, each head's Q blocks last-first under the causal mask.
+//    range [x*nwg/8, (x+1)*nwg/8)): without the mask, one head at a time, so
+//    that the blocks running at once on an XCD stream the same K/V through
+//    its L2; under the mask (BH not a multiple of 8), heads two at a time,
+//    alternating between the pair, each head's Q blocks last-first.
 // The map is a bijection of [0, nwg) onto (bh, qblock) pairs; under the
 // mask, qblock is the block's position in longest-first order (Tr - 1 is
 // the longest for a forward Q block).
@@ -214,6 +216,11 @@ FA_HD void map_workgroup(int wg, int BH, int Tr, bool causal, int &bh, int &qblo
     if ((nwg & 7) == 0) {
         const int per_xcd = nwg >> 3;
         work = (wg & 7) * per_xcd + (wg >> 3);
+    }
+    if (!causal) {  // equal blocks: one head at a time, its blocks sharing its K/V in L2
+        bh = work / Tr;
+        qblock = work - bh * Tr;
+        return;
     }
     const int pair = work / (2 * Tr);
     const int within = work - pair * 2 * Tr;

@@ -210,6 +210,23 @@ def test_workgroup_order_groups_heads_by_xcd(fa):
     assert fa.fa_map_workgroup(0, BH, Tr, False) == (0, 0)
 
 
+@pytest.mark.parametrize("BH,Tr", [(32, 128), (128, 32), (8, 3), (24, 33)])
+def test_non_causal_order_is_one_head_at_a_time(fa, BH, Tr):
+    """Without the mask every Q block has the same length: XCD x walks its
+    heads one at a time, each head's blocks in order, so the blocks running
+    at once share that head's K/V in the XCD's L2."""
+    nwg = BH * Tr
+    if nwg % 8:
+        seq = [fa.fa_map_workgroup(wg, BH, Tr, False) for wg in range(nwg)]
+        assert seq == [(h, b) for h in range(BH) for b in range(Tr)]
+        return
+    per_xcd = nwg // 8
+    for x in range(8):
+        seq = [fa.fa_map_workgroup(8 * w + x, BH, Tr, False) for w in range(per_xcd)]
+        flat = [bh * Tr + qb for bh, qb in seq]
+        assert flat == list(range(x * per_xcd, (x + 1) * per_xcd))
+
+
 @pytest.mark.parametrize("BH,Tr", [(128, 32), (512, 16), (32, 128), (24, 33), (8, 3)])
 def test_causal_order_phases_and_head_groups(fa, BH, Tr):
     """Causal order on each XCD: first the Q blocks >= Tr/4 four heads at a
