@@ -117,6 +117,32 @@ def measured_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def paged_bytes(w, lens, table_entries):
+    """K and V rows of every key read once, q read and out written once,
+    lse written, the block table and the lengths read."""
+    keys = sum(max(0, int(n)) for n in lens)
+    return float(2 * 2 * w.H * w.d * keys + 2 * 2 * w.B * w.H * w.d + 4 * w.B * w.H + 4 * table_entries + 4 * w.B)
+
+
+def varlen_bytes(w, lq, lk):
+    """q, k, v read once, out and lse written once."""
+    return float(2 * w.H * w.d * (2 * sum(lq) + 2 * sum(lk)) + 4 * w.H * sum(lq))
+
+
+def algorithmic_bytes(workload: str):
+    """Algorithmic bytes of one step of a workload (None if unknown)."""
+    import fa_inputs
+    if workload in fa_inputs.WORKLOADS:
+        return workload_bytes(fa_inputs.WORKLOADS[workload])
+    if workload in fa_inputs.PAGED_WORKLOADS:
+        w = fa_inputs.PAGED_WORKLOADS[workload]
+        return paged_bytes(w, fa_inputs.paged_lengths(w), w.B * -(-w.max_len // w.block_size))
+    if workload in fa_inputs.VARLEN_WORKLOADS:
+        w = fa_inputs.VARLEN_WORKLOADS[workload]
+        return varlen_bytes(w, *fa_inputs.varlen_lengths(w))
+    return None
+
+
 def check_fields(o, l, ref_o, ref_l, what: str):
     """max and mean |dO| and max |dLSE| of GPU outputs against the oracle's
     on the rows the oracle computed (a row without keys must give O = 0 and
@@ -233,7 +259,10 @@ def environment():
 
 def time_steps(step, steps, warmup, prewarm_s):
     """(ms per step over the timed region, mean per-step kernel ms from the
-    events, {median, min} of those per-step times)."""
+    events, {median, min} of those per-step times).  The K timed steps run
+    back to back between two synchronisations; the per-step events are
+    recorded in a second pass of K steps, so that recording them adds
+    nothing to the timed region (it matters for kernels of a few us)."""
     import torch
     dev = torch.device("cuda:0")
     t_end = time.perf_counter() + prewarm_s
@@ -244,16 +273,18 @@ def time_steps(step, steps, warmup, prewarm_s):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     stream = torch.cuda.current_stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for s, e in ev:
         s.record(stream)
         step()
         e.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     t = sorted(s.elapsed_time(e) for s, e in ev)
     n = len(t)
     spread = {"kernel_ms_median": t[n // 2] if n % 2 else 0.5 * (t[n // 2 - 1] + t[n // 2]), "kernel_ms_min": t[0]}
@@ -381,11 +412,9 @@ def run_paged_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s):
         fa.fa_fwd_paged_decode(qd, kcd, vcd, td, ld, w.num_splits, scale=w.scale, workspace=ws, out=out, lse=lse)
 
     ms_per_step, kernel_ms, spread = time_steps(step, steps, warmup, prewarm_s)
-    es = 2
     keys = int(lens.clamp(min=0).sum())
     flops = 4.0 * w.H * w.d * keys
-    nbytes = float(2 * es * w.H * w.d * keys + 2 * es * w.B * w.H * w.d + 4 * w.B * w.H
-                   + 4 * table.numel() + 4 * w.B)
+    nbytes = paged_bytes(w, lens.tolist(), table.numel())
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(name)}
@@ -440,7 +469,7 @@ def run_varlen_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s):
     lq = (cq[1:] - cq[:-1]).tolist()
     lk = (ck[1:] - ck[:-1]).tolist()
     flops = 4.0 * w.d * w.H * varlen_pairs(w, lq, lk)
-    nbytes = float(2 * w.H * w.d * (2 * sum(lq) + 2 * sum(lk)) + 4 * w.H * sum(lq))
+    nbytes = varlen_bytes(w, lq, lk)
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     rec = {
         "metric": "attention fwd TFLOP/s (and % of MI355X bf16 MFMA/HBM roofline) per config",
@@ -594,9 +623,12 @@ def summarize_rocprof(root: str, workload: str, out_dir: str, kernel: str = None
         lines += ["Counters of `%s` (`--pmc`, one pass per group, averaged over its dispatches):" % pattern, ""]
         grbm = c.get("GRBM_GUI_ACTIVE")
         per_xcd = grbm / 8.0 if grbm else None
-        if per_xcd and dur:
+        if per_xcd and dur and dur >= 100.0:
             lines.append("- GRBM_GUI_ACTIVE per XCD: %.0f cycles over a %.0f us dispatch -> %.2f GHz effective clock"
                          % (per_xcd, dur, per_xcd / dur / 1e3))
+        elif per_xcd and dur:
+            lines.append("- GRBM_GUI_ACTIVE per XCD: %.0f cycles over a %.0f us dispatch (too short to read a clock "
+                         "from; busy fractions below use these cycles)" % (per_xcd, dur))
         if per_xcd and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
             lines.append("- MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs)): %.1f %%"
                          % (100.0 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (per_xcd * 1024)))
@@ -619,10 +651,7 @@ def summarize_rocprof(root: str, workload: str, out_dir: str, kernel: str = None
         fs = COPY_BYTES / 1024.0 / cf["FETCH_SIZE"]
         ws = COPY_BYTES / 1024.0 / cw["WRITE_SIZE"]
         traffic = (c["FETCH_SIZE"] * fs + c["WRITE_SIZE"] * ws) * 1024.0
-        import fa_inputs
-        alg = None
-        if workload in fa_inputs.WORKLOADS:
-            alg = workload_bytes(fa_inputs.WORKLOADS[workload])
+        alg = algorithmic_bytes(workload)
         lines.append("- FETCH_SIZE %.0f KiB, WRITE_SIZE %.0f KiB per dispatch; copy calibration (1 GiB copy) "
                      "reads back FETCH x%.4f, WRITE x%.4f" % (c["FETCH_SIZE"], c["WRITE_SIZE"], fs, ws))
         lines.append("- HBM traffic per launch of `%s` (calibrated): %.4f GB%s" % (

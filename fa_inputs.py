@@ -116,6 +116,21 @@ PAGED_WORKLOADS = {
 }
 
 
+def _paged_lengths(w: PagedWorkload, g):
+    if w.lens == "full":
+        return [w.max_len] * w.B
+    bs = w.block_size
+    edge = [0, 1, bs - 1, bs + 1, w.max_len]
+    rest = torch.randint(1, w.max_len + 1, (w.B,), generator=g).tolist()
+    return [min(w.max_len, x) for x in (edge + rest)[:w.B]]
+
+
+def paged_lengths(w: PagedWorkload):
+    """The sequence lengths make_paged draws (the first draws of its
+    generator), without the caches."""
+    return _paged_lengths(w, torch.Generator().manual_seed(int(w.seed)))
+
+
 def make_paged(w: PagedWorkload):
     """(q, k_cache, v_cache, block_table, seq_lens) on the CPU.
 
@@ -138,12 +153,7 @@ def make_paged(w: PagedWorkload):
     g = torch.Generator().manual_seed(int(w.seed))
     bs = w.block_size
     max_blocks = -(-w.max_len // bs)
-    if w.lens == "full":
-        lens = [w.max_len] * w.B
-    else:
-        edge = [0, 1, bs - 1, bs + 1, w.max_len]
-        rest = torch.randint(1, w.max_len + 1, (w.B,), generator=g).tolist()
-        lens = [min(w.max_len, x) for x in (edge + rest)[:w.B]]
+    lens = _paged_lengths(w, g)
     need = [-(-n // bs) for n in lens]
     num_blocks = sum(need) + w.spare_blocks
     perm = torch.randperm(max(num_blocks, 1), generator=g).tolist()
@@ -209,6 +219,22 @@ VARLEN_WORKLOADS = {
 }
 
 
+def _varlen_lengths(w: VarlenWorkload, g):
+    def lengths():
+        x = torch.randint(w.min_len, w.max_len + 1, (w.S,), generator=g).tolist()
+        if w.edge:
+            x = ([0, 1, 127, 128, 129, w.max_len] + x)[:w.S]
+        return x
+    lq = lengths()
+    return lq, (lq if w.same_kv else lengths())
+
+
+def varlen_lengths(w: VarlenWorkload):
+    """(query lengths, key lengths) as make_varlen draws them (the first
+    draws of its generator), without the tensors."""
+    return _varlen_lengths(w, torch.Generator().manual_seed(int(w.seed)))
+
+
 def make_varlen(w: VarlenWorkload):
     """(q, k, v, cu_seqlens_q, cu_seqlens_k) on the CPU.
 
@@ -220,14 +246,7 @@ def make_varlen(w: VarlenWorkload):
     int32 cumulative sums starting at 0.
     """
     g = torch.Generator().manual_seed(int(w.seed))
-
-    def lengths():
-        x = torch.randint(w.min_len, w.max_len + 1, (w.S,), generator=g).tolist()
-        if w.edge:
-            x = ([0, 1, 127, 128, 129, w.max_len] + x)[:w.S]
-        return x
-    lq = lengths()
-    lk = lq if w.same_kv else lengths()
+    lq, lk = _varlen_lengths(w, g)
     cq = torch.tensor([0] + lq, dtype=torch.int64).cumsum(0).to(torch.int32)
     ck = torch.tensor([0] + lk, dtype=torch.int64).cumsum(0).to(torch.int32)
     q = torch.randn((int(cq[-1]), w.H, w.d), generator=g, dtype=torch.float32)
