@@ -7,16 +7,19 @@ decode workload; ``fa_fwd_paged_decode`` for the paged-cache decode) over one
 batch of seeded synthetic inputs already resident in device memory.  The GPU's clock ramps up over the first tens of
 milliseconds of sustained load after idle, so untimed steps run for at least
 ``--prewarm-s`` seconds (0.3 by default) before the W untimed warmup steps;
-then K timed steps are bracketed by ``torch.cuda.synchronize()``.  Each step
-is also bracketed by events on the stream the kernels run on, which gives
-the per-launch kernel time used for the roofline fraction.
+then K timed steps run back to back between two ``torch.cuda.synchronize()``
+calls.  A second pass of K steps, each between events on the stream the
+kernels run on, gives the per-launch kernel time used for the roofline
+fraction.
 
 By default (``--workload configs``) the five configurations are timed in
 turn, one JSON line each: single-head fp32, ragged causal fp16, long
 non-causal bf16, single-token decode, and last the causal bf16 prefill
 B=8, H=16, N=4096, d=128, so that the final line is the headline.
 ``--workload all`` adds the backward, FP8, paged-decode and variable-length
-workloads before the headline.  FLOPs follow the convention 4*B*H*Nq*Nk*d
+workloads before the headline.  ``--workload gemm_bf16_n8192`` times a
+plain bf16 GEMM by the vendor library instead, the practical matrix-core
+rate at the clock the power limit allows.  FLOPs follow the convention 4*B*H*Nq*Nk*d
 (the two contractions), halved under the causal mask; bytes are one read of
 Q, K, V and one write of O and LSE.
 
@@ -61,9 +64,17 @@ KERNEL_SOURCES = {
 }
 
 
+# Reference GEMM: a square bf16 product by the vendor library (torch.matmul,
+# hipBLASLt), the practical matrix-core rate under the GPU's power limit.
+GEMM_WORKLOAD = "gemm_bf16_n8192"
+GEMM_N = 8192
+
+
 def workload_kernel(name: str):
     """(source family, name pattern of the dominant kernel) of a workload."""
     import fa_inputs
+    if name == GEMM_WORKLOAD:
+        return "gemm", "Cijk"
     if name in fa_inputs.PAGED_WORKLOADS:
         return "decode", "splitkv_partial"
     if name in fa_inputs.VARLEN_WORKLOADS:
@@ -132,6 +143,8 @@ def varlen_bytes(w, lq, lk):
 def algorithmic_bytes(workload: str):
     """Algorithmic bytes of one step of a workload (None if unknown)."""
     import fa_inputs
+    if workload == GEMM_WORKLOAD:
+        return 3 * GEMM_N * GEMM_N * 2
     if workload in fa_inputs.WORKLOADS:
         return workload_bytes(fa_inputs.WORKLOADS[workload])
     if workload in fa_inputs.PAGED_WORKLOADS:
@@ -532,6 +545,39 @@ def copy_probe(nbytes: int, steps: int) -> int:
     return 0
 
 
+def gemm_ceiling(steps: int, warmup: int, prewarm_s: float) -> int:
+    """The reference GEMM (GEMM_WORKLOAD): C = A B with A, B [n, n] bf16 by
+    torch.matmul, timed like the attention steps (pre-warm, warmup, K steps
+    between events).  Its rate is the matrix-core throughput the vendor
+    library reaches on this GPU at the clock its power limit allows."""
+    import torch
+    n = GEMM_N
+    g = torch.Generator(device="cpu").manual_seed(1)
+    a = torch.randn(n, n, generator=g).to(torch.bfloat16).to("cuda:0")
+    b = torch.randn(n, n, generator=g).to(torch.bfloat16).to("cuda:0")
+    c = torch.empty(n, n, dtype=torch.bfloat16, device="cuda:0")
+    t_end = time.perf_counter() + prewarm_s
+    while time.perf_counter() < t_end:
+        torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+    for _ in range(warmup):
+        torch.matmul(a, b, out=c)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    tflops = 2.0 * n ** 3 / ms / 1e9
+    print(json.dumps({"metric": "gemm_tflops", "value": round(tflops, 1), "unit": "TFLOP/s", "ms_per_gemm": ms,
+                      "steps": steps, "warmup": warmup, "dtype": "bf16", "config": {"workload": GEMM_WORKLOAD},
+                      "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4), "environment": environment()}),
+          flush=True)
+    return 0
+
+
 # The rocprofv3 passes --summarize-rocprof reads, one directory each under
 # DIR, with the command that fills it (run from the repository root).
 PROFILE_PASSES = {
@@ -666,7 +712,7 @@ def summarize_rocprof(root: str, workload: str, out_dir: str, kernel: str = None
     md = "%s_%s.md" % (pattern, workload)
     with open(os.path.join(out_dir, md), "w") as f:
         f.write("\n".join(lines) + "\n")
-    if traffic is not None and dominant:
+    if traffic is not None and dominant and family in KERNEL_SOURCES:
         rec = {"workload": workload, "kernel": pattern, "kernel_source_hash": kernel_source_hash(family),
                "fetch_kib_per_dispatch": c["FETCH_SIZE"], "write_kib_per_dispatch": c["WRITE_SIZE"],
                "copy_fetch_scale": fs, "copy_write_scale": ws, "hbm_bytes_per_launch": traffic,
@@ -685,7 +731,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="configs",
-                    help="configs (the five configurations, headline last), all, or one workload name")
+                    help="configs (the five configurations, headline last), all, one workload name, or "
+                         "gemm_bf16_n8192 (the reference GEMM)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target oracle time for each line's cpu_baseline")
@@ -716,6 +763,8 @@ def main():
         return 2
     if args.copy_bytes:
         return copy_probe(args.copy_bytes, args.steps)
+    if args.workload == GEMM_WORKLOAD:
+        return gemm_ceiling(args.steps, args.warmup, args.prewarm_s)
     import fa_inputs
     if args.workload == "configs":
         names = list(CONFIG_WORKLOADS)
