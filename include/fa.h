@@ -125,6 +125,12 @@ typedef enum fa_status {
  * The environment variable FA_PREFILL_SPLIT overrides the first choice: 0
  * or 1 never splits, n >= 2 asks for n chunks (capped at the tile count);
  * FA_PREFILL_SHAPE forces a tile shape (sweeps).
+ * float32 runs the vector-ALU kernel over (batch*head, Q block of 64)
+ * workgroups; a grid of fewer than 256 cuts each Q block's key range into
+ * min(ceil(512 / grid), 64) chunks of whole 32-key blocks (fewer where
+ * whole-block chunks need fewer), merged by the same combine through the
+ * same workspace.  FA_F32_SPLIT overrides that choice as FA_PREFILL_SPLIT
+ * does.
  */
 int fa_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
            int B, int H, int Nq, int Nk, int d, float scale, int causal,
@@ -134,7 +140,8 @@ int fa_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
  * fa_fwd_noalloc -- fa_fwd for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same arguments, checks and dispatch as fa_fwd, but the
- * split workspace (decode, and prefill grids too small for the GPU) is a
+ * split workspace (decode, and prefill grids too small for the GPU, float32
+ * included) is a
  * static device array of FA_NOALLOC_SCRATCH_BYTES bytes instead of the
  * library cache, and the call allocates nothing.  Each GPU the library runs
  * on holds its own copy of that array until the process ends; its address is

@@ -235,9 +235,21 @@ int forward(const void *q, const void *k, const void *v, void *out, float *lse, 
         return run_splitkv(q, k, v, out, lse, B, H, Nk, d, scale, S, ws, dtype, stream);
     }
     const float sl = (float)((double)scale * kLog2e);
-    if (dtype == FA_F32)
-        return hip_status(fa::launch_prefill_f32(d, causal == 1, q, k, v, out, lse, B * H, Nq, Nk, sl, stream),
-                          "fp32 prefill launch");
+    if (dtype == FA_F32) {  // a grid too small for the GPU splits its key range, then combines
+        int S = fa::f32_split_count(causal == 1, B * H, Nq, Nk);
+        if (S > 1 && scratch_src) {
+            const int fit = scratch_max_splits(B, H, Nq, d);
+            if (fit < S) S = fit >= 2 ? fa::f32_split_normalise(causal == 1, Nq, Nk, fit) : 1;
+        }
+        void *ws = nullptr;
+        if (S > 1) {
+            st = take(workspace_bytes(B, H, Nq, d, S), &ws);
+            if (st != FA_OK) return st;
+        }
+        return hip_status(
+            fa::launch_prefill_f32(d, causal == 1, q, k, v, out, lse, B * H, Nq, Nk, sl, S, ws, stream),
+            "fp32 prefill launch");
+    }
     int shape = prefill_shape(d);
     int S = fa::prefill_split_count(d, causal == 1, shape, B * H, Nq, Nk);
     if (S > 1 && scratch_src) {

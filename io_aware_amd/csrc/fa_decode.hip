@@ -356,9 +356,10 @@ hipError_t launch_combine(int dtype, int d, const float *ws_o, const float *ws_l
 #define FA_CASE(DD)                                                                                      \
     case DD:                                                                                             \
         if (dtype == 2) hipLaunchKernelGGL((splitkv_combine_kernel<__bf16, DD>), grid, dim3(256), 0, stream, b); \
-        else hipLaunchKernelGGL((splitkv_combine_kernel<_Float16, DD>), grid, dim3(256), 0, stream, b);          \
+        else if (dtype == 1) hipLaunchKernelGGL((splitkv_combine_kernel<_Float16, DD>), grid, dim3(256), 0, stream, b); \
+        else hipLaunchKernelGGL((splitkv_combine_kernel<float, DD>), grid, dim3(256), 0, stream, b);             \
         return hipGetLastError();
-    if (dtype != 1 && dtype != 2) return hipErrorInvalidValue;
+    if (dtype != 0 && dtype != 1 && dtype != 2) return hipErrorInvalidValue;
     switch (d) {
         FA_CASE(32)
         FA_CASE(64)

@@ -15,10 +15,22 @@
 // M = max(m1, m2), l = l1 e^(m1-M) + l2 e^(m2-M), o likewise; then O = o / l
 // and LSE = M + ln l.  Every product and sum is a float32 FMA; exp is exp2
 // with scale*log2(e) folded in.
+//
+// A grid of fewer workgroups than the GPU has CUs leaves most of it idle
+// while each workgroup walks its whole key range on one CU.  Such grids are
+// split along the keys (split-KV, section 11 of the first page): workgroup
+// (row block, chunk) walks one chunk of whole 32-key blocks and writes its
+// normalised partial o / l and its logsumexp to a workspace, and the
+// split-KV combine merges the chunks.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "fa_internal.h"
+
+#ifndef FA_F32_SPLIT_BLOCK
+#define FA_F32_SPLIT_BLOCK 32
+#endif
 
 namespace fa {
 namespace {
@@ -36,6 +48,11 @@ struct F32Args {
     int Nq;
     int Nk;
     int Tr;  // 64-row Q blocks per (batch, head)
+    // split launch: chunk c covers keys [c * chunk, (c + 1) * chunk)
+    float *ws_o;    // [BH * Nq, S, D] normalised partials
+    float *ws_lse;  // [BH * Nq, S] their logsumexp (natural log)
+    int S;
+    int chunk;      // keys per chunk, a multiple of the split block
     float scale_log2;  // |scale| * log2(e) (1 for a zero scale; see FoldedScale)
     uint32_t qflip;    // sign bit flipped in Q for a negative scale
     uint32_t qkeep;    // 0 zeroes Q for a zero scale
@@ -46,12 +63,18 @@ struct F32Args {
 template <int D>
 constexpr int f32_waves() { return D <= 32 ? 16 : (D <= 64 ? 8 : 4); }
 
-template <int D, bool CAUSAL>
+// Keys per K/V block of a split launch: chunks are whole blocks, so a short
+// key range still splits over many workgroups (32 measured best against 16
+// and 64 on short and long ranges).
+constexpr int kSplitBlock = FA_F32_SPLIT_BLOCK;
+
+template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(f32_waves<D>() * 64) void prefill_f32_kernel(F32Args a) {
     constexpr int NW = f32_waves<D>();
     constexpr int BR = 64;
-    constexpr int BC = 64;
+    constexpr int BC = SPLIT ? kSplitBlock : 64;
     constexpr int KPW = BC / NW;  // keys of a block per wave
+    static_assert(BC % NW == 0, "every wave takes the same number of keys of a block");
     constexpr int C4 = D / 4;     // float4 chunks per row
     constexpr int KV_FLOATS = 2 * BC * D;                 // one K and one V block
     constexpr int MERGE_FLOATS = (NW / 2) * 64 * (D + 2);  // the upper half's (m, l, o) of a merge round
@@ -63,8 +86,13 @@ __global__ __launch_bounds__(f32_waves<D>() * 64) void prefill_f32_kernel(F32Arg
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int bh = blockIdx.x / a.Tr;
-    const int q0 = (blockIdx.x - bh * a.Tr) * BR;
+    int wg = blockIdx.x, chunk_idx = 0;
+    if constexpr (SPLIT) {  // the chunks of one row block are neighbours
+        chunk_idx = wg % a.S;
+        wg /= a.S;
+    }
+    const int bh = wg / a.Tr;
+    const int q0 = (wg - bh * a.Tr) * BR;
     const int row = q0 + lane;
     const int Nq = a.Nq;
     const int Nk = a.Nk;
@@ -91,7 +119,10 @@ __global__ __launch_bounds__(f32_waves<D>() * 64) void prefill_f32_kernel(F32Arg
     float l = 0.f;
 
     const int kv_end = CAUSAL ? min(Nk, q0 + BR) : Nk;
-    for (int k0 = 0; k0 < kv_end; k0 += BC) {
+    // keys [kbeg, kend): all visible ones, or one chunk (workgroup-uniform)
+    const int kbeg = SPLIT ? min(kv_end, chunk_idx * a.chunk) : 0;
+    const int kend = SPLIT ? min(kv_end, kbeg + a.chunk) : kv_end;
+    for (int k0 = kbeg; k0 < kend; k0 += BC) {
         __syncthreads();  // the previous block's reads are done
         for (int idx = tid; idx < BC * C4; idx += NW * 64) {
             const int key = k0 + idx / C4;
@@ -174,21 +205,35 @@ __global__ __launch_bounds__(f32_waves<D>() * 64) void prefill_f32_kernel(F32Arg
         }
     }
 
+    // (split launch: this chunk's o / l and logsumexp, -inf with o = 0 where
+    // the chunk holds no visible key of the row)
     if (wave == 0 && row < Nq) {
         const float inv = (l > 0.f) ? 1.f / l : 0.f;
-        float *op = a.out + (size_t)bh * Nq * D + (size_t)row * D;
+        const float lse_row = (l > 0.f) ? (m + __builtin_amdgcn_logf(l)) * kLn2f : -__builtin_inff();
+        const size_t slot = SPLIT ? ((size_t)bh * Nq + row) * a.S + chunk_idx : 0;
+        float *op = SPLIT ? a.ws_o + slot * D : a.out + (size_t)bh * Nq * D + (size_t)row * D;
 #pragma unroll
         for (int t = 0; t < D; t += 4)
             *reinterpret_cast<f32x4 *>(op + t) = f32x4{o[t] * inv, o[t + 1] * inv, o[t + 2] * inv, o[t + 3] * inv};
-        if (a.lse != nullptr)
-            a.lse[(size_t)bh * Nq + row] = (l > 0.f) ? (m + __builtin_amdgcn_logf(l)) * kLn2f : -__builtin_inff();
+        if (SPLIT)
+            a.ws_lse[slot] = lse_row;
+        else if (a.lse != nullptr)
+            a.lse[(size_t)bh * Nq + row] = lse_row;
     }
+}
+
+// kSplitBlock-key blocks of the key range a split cuts (under the mask, the
+// last row block's range; chunks past a row block's range are empty)
+int f32_key_blocks(bool causal, int Nq, int Nk) {
+    const long long rows = (long long)(Nq + 63) / 64 * 64;
+    const int kext = causal && rows < Nk ? (int)rows : Nk;
+    return (kext + kSplitBlock - 1) / kSplitBlock;
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_f32_one(const void *q, const void *k, const void *v, void *out, float *lse, int BH, int Nq,
-                          int Nk, float sl, hipStream_t stream) {
-    F32Args a;
+                          int Nk, float sl, int S, void *workspace, hipStream_t stream) {
+    F32Args a = {};
     a.q = static_cast<const float *>(q);
     a.k = static_cast<const float *>(k);
     a.v = static_cast<const float *>(v);
@@ -201,20 +246,64 @@ hipError_t launch_f32_one(const void *q, const void *k, const void *v, void *out
     a.scale_log2 = fs.c;
     a.qflip = fs.flip;
     a.qkeep = fs.keep;
-    const long long nwg = (long long)BH * a.Tr;
+    if (S > 1) {
+        if (S > f32_key_blocks(CAUSAL, Nq, Nk) || workspace == nullptr) return hipErrorInvalidValue;
+        a.S = S;
+        a.chunk = (f32_key_blocks(CAUSAL, Nq, Nk) + S - 1) / S * kSplitBlock;
+        a.ws_o = static_cast<float *>(workspace);
+        a.ws_lse = a.ws_o + (size_t)BH * Nq * S * D;
+    }
+    const long long nwg = (long long)BH * a.Tr * (S > 1 ? S : 1);
     if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((prefill_f32_kernel<D, CAUSAL>), dim3((unsigned)nwg), dim3(f32_waves<D>() * 64), 0, stream, a);
-    return hipGetLastError();
+    if (S > 1)
+        hipLaunchKernelGGL((prefill_f32_kernel<D, CAUSAL, true>), dim3((unsigned)nwg), dim3(f32_waves<D>() * 64), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((prefill_f32_kernel<D, CAUSAL, false>), dim3((unsigned)nwg), dim3(f32_waves<D>() * 64),
+                           0, stream, a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || S < 2) return err;
+    return launch_combine(0, D, a.ws_o, a.ws_lse, out, lse, BH * Nq, S, stream);
 }
 
 }  // namespace
 
+int f32_split_normalise(bool causal, int Nq, int Nk, int S) {
+    const int blocks = f32_key_blocks(causal, Nq, Nk);
+    S = S < blocks ? S : blocks;
+    if (S < 2) return 1;
+    // whole blocks per chunk; drop chunks that would start past the keys
+    const int per = (blocks + S - 1) / S;
+    return (blocks + per - 1) / per;
+}
+
+int f32_split_count(bool causal, int BH, int Nq, int Nk) {
+    if (BH < 1 || Nq < 1 || Nk < 1) return 1;
+    const long long grid = (long long)BH * ((Nq + 63) / 64);
+    int S;
+    const char *env = getenv("FA_F32_SPLIT");
+    if (env != nullptr && env[0] != '\0') {
+        S = atoi(env);  // 0 or 1: never split; n: at most n chunks
+    } else {
+        // Split while the grid is below one workgroup per CU: every 64 keys
+        // of a workgroup's range cost several microseconds of vector-ALU
+        // work on its CU, against a few for the combine launch.  Aim for two
+        // workgroups per CU, at most 64 chunks.
+        constexpr long long kCUs = 256;
+        if (grid >= kCUs) return 1;
+        S = (int)((2 * kCUs + grid - 1) / grid);
+        S = S < 64 ? S : 64;
+    }
+    return f32_split_normalise(causal, Nq, Nk, S);
+}
+
 hipError_t launch_prefill_f32(int d, bool causal, const void *q, const void *k, const void *v, void *out,
-                              float *lse, int BH, int Nq, int Nk, float sl, hipStream_t stream) {
-#define FA_CASE(DD)                                                                           \
-    case DD:                                                                                  \
-        return causal ? launch_f32_one<DD, true>(q, k, v, out, lse, BH, Nq, Nk, sl, stream)   \
-                      : launch_f32_one<DD, false>(q, k, v, out, lse, BH, Nq, Nk, sl, stream);
+                              float *lse, int BH, int Nq, int Nk, float sl, int S, void *workspace,
+                              hipStream_t stream) {
+#define FA_CASE(DD)                                                                                             \
+    case DD:                                                                                                    \
+        return causal ? launch_f32_one<DD, true>(q, k, v, out, lse, BH, Nq, Nk, sl, S, workspace, stream)       \
+                      : launch_f32_one<DD, false>(q, k, v, out, lse, BH, Nq, Nk, sl, S, workspace, stream);
     switch (d) {
         FA_CASE(32)
         FA_CASE(64)

@@ -93,10 +93,18 @@ hipError_t launch_prefill_split(int dtype, int d, bool causal, int shape, const 
 hipError_t launch_combine(int dtype, int d, const float *ws_o, const float *ws_lse, void *out, float *lse,
                           int rows, int S, hipStream_t stream);
 
-// float32 tiled forward (vector ALU), Br = Bc = 64.
+// float32 tiled forward (vector ALU), Br = Bc = 64.  With S > 1 the key
+// range is cut into S chunks of whole 32-key blocks, one workgroup each,
+// written to workspace in the split layout above (S * (d + 1) floats per
+// row) and merged by the combine.  f32_split_count chooses S for a grid
+// (1: no split; FA_F32_SPLIT = 0 disables, n >= 2 asks for at most n chunks);
+// f32_split_normalise gives the count a launch runs with for at most S.
+int f32_split_count(bool causal, int BH, int Nq, int Nk);
+int f32_split_normalise(bool causal, int Nq, int Nk, int S);
 hipError_t launch_prefill_f32(int d, bool causal, const void *q, const void *k,
                               const void *v, void *out, float *lse, int BH,
-                              int Nq, int Nk, float scale_log2, hipStream_t stream);
+                              int Nq, int Nk, float scale_log2, int S, void *workspace,
+                              hipStream_t stream);
 
 // Split-KV decode: stage one (per chunk partials into the workspace) then
 // stage two (logsumexp-weighted combine).  dtype FA_F16 or FA_BF16; Nq == 1.

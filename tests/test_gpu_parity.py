@@ -128,8 +128,10 @@ def test_ragged_shapes(fa, dtype, d, causal, split, monkeypatch):
     below the split threshold), "never" keeps one workgroup per Q block."""
     if split == "never":
         monkeypatch.setenv("FA_PREFILL_SPLIT", "0")
+        monkeypatch.setenv("FA_F32_SPLIT", "0")
     else:
         monkeypatch.delenv("FA_PREFILL_SPLIT", raising=False)
+        monkeypatch.delenv("FA_F32_SPLIT", raising=False)
     for i, (B, H, Nq, Nk) in enumerate(SHAPES):
         run_full(fa, B, H, Nq, Nk, d, dtype, causal, seed=100 + i + 10 * d,
                  label="B%d H%d Nq%d Nk%d d%d %s causal=%d split=%s" % (B, H, Nq, Nk, d, dtype, causal, split))
@@ -179,6 +181,42 @@ def test_split_prefill_automatic_choice(fa, B, H, Nq, Nk, d, dtype, causal, chun
     qd, kd, vd = to_dev(q, k, v)
     auto = fa.fa_fwd(qd, kd, vd, causal=causal)
     monkeypatch.setenv("FA_PREFILL_SPLIT", str(chunks))
+    forced = fa.fa_fwd(qd, kd, vd, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(auto[0], forced[0]) and torch.equal(auto[1], forced[1])
+
+
+@pytest.mark.parametrize("split", ["0", "2", "3", "7", "64"])
+def test_f32_split_chunk_counts(fa, split, monkeypatch):
+    """The float32 path with its key range cut into at most n chunks of
+    whole 32-key blocks (0: never split; 64 is capped at one block per
+    chunk), then combined: ragged key counts, both masks, keys below and
+    above the query count (chunks past a causal row block's keys are
+    empty), every head dim; max |dO| <= 1e-5 as for the unsplit path."""
+    monkeypatch.setenv("FA_F32_SPLIT", split)
+    cases = [(1, 1, 256, 256, 64, False), (1, 2, 300, 517, 32, True), (2, 1, 517, 300, 128, True),
+             (1, 1, 129, 1000, 64, True), (1, 3, 70, 700, 128, False), (1, 1, 1, 200, 64, False)]
+    for i, (B, H, Nq, Nk, d, causal) in enumerate(cases):
+        run_full(fa, B, H, Nq, Nk, d, "f32", causal, seed=820 + i,
+                 label="f32 split=%s B%d H%d Nq%d Nk%d d%d causal=%d" % (split, B, H, Nq, Nk, d, causal))
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,d,causal,chunks", [
+    (1, 1, 256, 256, 64, False, 8),     # the single-head workload: grid 4, 8 blocks: one block per chunk
+    (1, 2, 300, 5000, 32, False, 40),   # grid 10: 52 chunks wanted, 157 blocks: 40 chunks of 4 blocks
+    (4, 64, 64, 512, 64, True, 1),      # grid 256: no split
+])
+def test_f32_split_automatic_choice(fa, B, H, Nq, Nk, d, causal, chunks, monkeypatch):
+    """Without FA_F32_SPLIT a float32 grid below 256 workgroups is split
+    into min(ceil(512 / grid), 64) chunks of whole 32-key blocks (then as
+    many as whole-block chunks need): parity with the oracle, and bitwise
+    the result of asking for that chunk count."""
+    monkeypatch.delenv("FA_F32_SPLIT", raising=False)
+    q, k, v, _, _ = run_full(fa, B, H, Nq, Nk, d, "f32", causal, seed=840 + d,
+                             label="f32 auto split B%d H%d Nq%d Nk%d d%d causal=%d" % (B, H, Nq, Nk, d, causal))
+    qd, kd, vd = to_dev(q, k, v)
+    auto = fa.fa_fwd(qd, kd, vd, causal=causal)
+    monkeypatch.setenv("FA_F32_SPLIT", str(chunks))
     forced = fa.fa_fwd(qd, kd, vd, causal=causal)
     torch.cuda.synchronize()
     assert torch.equal(auto[0], forced[0]) and torch.equal(auto[1], forced[1])

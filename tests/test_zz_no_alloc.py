@@ -67,9 +67,13 @@ def test_split_prefill_then_smaller(fa):
     check_pair(fa, [(1, 1, 2500, 4000, 128), (1, 1, 700, 700, 128)], True, "f16", 3120, "split causal")
 
 
-def test_prefill_and_f32_need_no_scratch(fa):
+def test_prefill_without_scratch_and_f32_split(fa):
+    # a 16-bit grid that needs no split workspace; then float32 grids below
+    # one workgroup per CU, whose key ranges are split into chunks merged
+    # through the scratch (40 chunks of 4 blocks, then 3 of 1; causal: 8, then 4)
     check_pair(fa, [(2, 4, 1000, 1000, 128), (1, 2, 300, 517, 64)], True, "bf16", 3130, "prefill")
-    check_pair(fa, [(1, 1, 256, 256, 64), (1, 2, 100, 77, 32)], False, "f32", 3140, "f32")
+    check_pair(fa, [(1, 2, 300, 5000, 32), (1, 2, 100, 77, 32)], False, "f32", 3140, "f32")
+    check_pair(fa, [(1, 1, 256, 256, 64), (1, 1, 70, 130, 128)], True, "f32", 3150, "f32 causal")
 
 
 def test_split_too_large_for_the_scratch_takes_fewer_chunks(fa):
