@@ -61,13 +61,15 @@ def _replay_and_check(fa, g, inputs, outputs, eager, seeds, fresh):
             assert torch.equal(a, b), "replay with inputs of seed %d differs from the eager call" % seed
 
 
-@pytest.mark.parametrize("B,H,Nq,Nk,d,causal", [
-    (2, 4, 1000, 1000, 128, True),      # the tiled prefill
-    (4, 8, 1, 4096, 128, False),        # Nq = 1: split-KV decode with the library workspace
-    (1, 2, 300, 5000, 64, False),       # a grid too small for the GPU: split prefill + combine
+@pytest.mark.parametrize("B,H,Nq,Nk,d,causal,dtype", [
+    (2, 4, 1000, 1000, 128, True, "bf16"),     # the tiled prefill
+    (4, 8, 1, 4096, 128, False, "bf16"),       # Nq = 1: split-KV decode with the library workspace
+    (1, 2, 300, 5000, 64, False, "bf16"),      # a grid too small for the GPU: split prefill + combine
+    (1, 1, 256, 256, 64, False, "f32"),        # float32 small grid: key chunks + float32 combine
+    (1, 2, 200, 700, 32, True, "f32"),
 ])
-def test_forward_in_a_graph(fa, B, H, Nq, Nk, d, causal):
-    q, k, v = fa_inputs.make_qkv_device(B, H, Nq, Nk, d, "bf16", seed=40, device=DEV)
+def test_forward_in_a_graph(fa, B, H, Nq, Nk, d, causal, dtype):
+    q, k, v = fa_inputs.make_qkv_device(B, H, Nq, Nk, d, dtype, seed=40, device=DEV)
     out = torch.empty_like(q)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=DEV)
     g = _capture(lambda: fa.fa_fwd(q, k, v, causal=causal, out=out, lse=lse))
@@ -76,7 +78,7 @@ def test_forward_in_a_graph(fa, B, H, Nq, Nk, d, causal):
         return fa.fa_fwd(q, k, v, causal=causal)
 
     _replay_and_check(fa, g, (q, k, v), (out, lse), eager, (41, 42, 43),
-                      lambda s: fa_inputs.make_qkv_device(B, H, Nq, Nk, d, "bf16", seed=s, device=DEV))
+                      lambda s: fa_inputs.make_qkv_device(B, H, Nq, Nk, d, dtype, seed=s, device=DEV))
 
 
 def test_graph_survives_workspace_growth(fa):
