@@ -19,7 +19,7 @@ oracle.
   plus half a bf16 unit at |O|.  That worst case must stay below the bar,
   so the margin does not rest on how the roundings happen to fall.
 
-The figures are printed; the design doc quotes them.
+The figures are printed so that a run shows them.
 """
 import numpy as np
 import pytest
