@@ -49,3 +49,22 @@ def compare(out, lse, ref_o, ref_l, dtype, label):
 
 def to_dev(*ts):
     return [t.to(DEV).contiguous() for t in ts]
+
+
+def compare_grad(x, ref, dtype, label):
+    """A gradient against the fp64 backward oracle: per element
+    |d| / (|ref| + rms(ref)) and the mean |d| / rms(ref) within BWD_TOL."""
+    x = x.detach().float().cpu().numpy().astype(np.float64).reshape(ref.shape)
+    assert np.isfinite(x).all(), label + ": non-finite gradient"
+    err = np.abs(x - ref)
+    rms = float(np.sqrt((ref ** 2).mean()))
+    if rms == 0.0:
+        # an exactly-zero gradient (a single key: P = 1, dS = 0) comes out as
+        # float32 rounding noise of dP - D, far below 16-bit resolution
+        assert err.max() <= 1e-4, "%s: %.3e where the gradient is 0" % (label, err.max())
+        return
+    elem = (err / (np.abs(ref) + rms)).max()
+    max_tol, mean_tol = BWD_TOL[dtype]
+    note("%s: rms=%.3e max|d|=%.3e elem=%.3e mean/rms=%.3e" % (label, rms, err.max(), elem, err.mean() / rms))
+    assert elem <= max_tol, "%s: max |d|/(|ref|+rms) %.3e > %.3e" % (label, elem, max_tol)
+    assert err.mean() <= mean_tol * rms, "%s: mean |d| %.3e > %.1e * rms" % (label, err.mean(), mean_tol)

@@ -25,7 +25,7 @@ import torch
 
 import fa_inputs
 import oracle
-from parity_util import BWD_TOL, DEV, note, to_dev
+from parity_util import DEV, compare_grad, note, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -34,23 +34,6 @@ pytestmark = pytest.mark.gpu
 def fa():
     import io_aware_amd
     return io_aware_amd
-
-
-def compare_grad(x, ref, dtype, label):
-    x = x.detach().float().cpu().numpy().astype(np.float64).reshape(ref.shape)
-    assert np.isfinite(x).all(), label + ": non-finite gradient"
-    err = np.abs(x - ref)
-    rms = float(np.sqrt((ref ** 2).mean()))
-    if rms == 0.0:
-        # an exactly-zero gradient (a single key: P = 1, dS = 0) comes out as
-        # float32 rounding noise of dP - D, far below 16-bit resolution
-        assert err.max() <= 1e-4, "%s: %.3e where the gradient is 0" % (label, err.max())
-        return
-    elem = (err / (np.abs(ref) + rms)).max()
-    max_tol, mean_tol = BWD_TOL[dtype]
-    note("%s: rms=%.3e max|d|=%.3e elem=%.3e mean/rms=%.3e" % (label, rms, err.max(), elem, err.mean() / rms))
-    assert elem <= max_tol, "%s: max |d|/(|ref|+rms) %.3e > %.3e" % (label, elem, max_tol)
-    assert err.mean() <= mean_tol * rms, "%s: mean |d| %.3e > %.1e * rms" % (label, err.mean(), mean_tol)
 
 
 def run_bwd(fa, B, H, Nq, Nk, d, dtype, causal, seed, q_sigma=1.0, label=None):

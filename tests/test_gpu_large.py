@@ -1,5 +1,6 @@
-"""GPU parity beyond 2^31 elements per tensor: the dense forward and the
-split-KV decode index q, k, v and out with 64-bit offsets.  The tensors here
+"""GPU parity beyond 2^31 elements per tensor: the dense forward, the
+split-KV decode, the backward and the FP8 forward index their tensors with
+64-bit offsets.  The tensors here
 hold more than 2^31 elements (4 GiB and more in bf16); heads past element 2^31
 are compared with the fp64 oracle on sampled query rows (a head at a time:
 the oracle sees that head's K and V in full).
@@ -13,7 +14,8 @@ import torch
 
 import fa_inputs
 import oracle
-from parity_util import DEV, compare, note
+from oracle import fp8
+from parity_util import DEV, FP8_LSE, FP8_MAX, FP8_MEAN, compare, compare_grad, note
 
 pytestmark = pytest.mark.gpu
 
@@ -65,3 +67,48 @@ def test_decode_past_2_31_elements(fa):
         ref_o, ref_l = oracle.attention(q[b, h].cpu()[None, None], k[b, h].cpu()[None, None],
                                         v[b, h].cpu()[None, None], scale, False)
         compare(out[b, h], lse[b, h], ref_o.reshape(1, d), ref_l.reshape(1), "bf16", "decode head %d" % bh)
+
+
+def test_backward_past_2_31_elements(fa):
+    B, H, N, d = 33, 128, 4096, 128          # 33*128*4096*128 = 2^31 + 2^26 elements per tensor
+    assert B * H * N * d > 2 ** 31
+    note("case backward B%d H%d N%d d%d causal (sampled heads past element 2^31)" % (B, H, N, d))
+    q, k, v = fa_inputs.make_qkv_device(B, H, N, N, d, "bf16", seed=4444, device=DEV)
+    g = fa_inputs.make_qkv_device(B, H, N, 1, d, "bf16", seed=4445, device=DEV)[0]   # dO, Q-shaped
+    scale = fa_inputs.default_scale(d)
+    out, lse = fa.fa_fwd(q, k, v, scale=scale, causal=True)
+    dq, dk, dv = fa.fa_bwd(q, k, v, out, g, lse, scale=scale, causal=True)
+    torch.cuda.synchronize()
+    first_past = (2 ** 31) // (N * d)
+    rows = np.array([0, 1, 31, 32, 127, 128, 2047, 2048, 4094, 4095])
+    for bh in sorted({first_past, first_past + 1, B * H - 1}):
+        b, h = divmod(bh, H)
+        one = [t[b, h].cpu()[None, None] for t in (q, k, v, g)]
+        ref = oracle.attention_bwd(*one, scale, True, heads=np.array([0]), q_idx=rows, k_idx=rows)
+        r = torch.from_numpy(rows)
+        for name, x, rf in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+            compare_grad(x[b, h].cpu()[r][None], rf, "bf16", "backward head %d %s" % (bh, name))
+
+
+def test_fp8_past_2_31_elements(fa):
+    B, H, N, d = 33, 128, 4096, 128          # every bf16 input 2^31 + 2^26 elements, every code array as many bytes
+    assert B * H * N * d > 2 ** 31
+    note("case fp8 B%d H%d N%d d%d causal (sampled heads past element 2^31)" % (B, H, N, d))
+    q, k, v = fa_inputs.make_qkv_device(B, H, N, N, d, "bf16", seed=4646, device=DEV)
+    signs = fa_inputs.make_signs(d, 4646)
+    scale = fa_inputs.default_scale(d)
+    pack = fa.fa_quantize_fp8(q, k, v, signs=signs.to(DEV))
+    out, lse = fa.fa_fwd_fp8(pack, B, H, N, N, d, scale=scale, causal=True)
+    torch.cuda.synchronize()
+    first_past = (2 ** 31) // (N * d)
+    rows = np.array([0, 1, 63, 64, 127, 128, 2047, 2048, 4094, 4095])
+    for bh in sorted({first_past, first_past + 1, B * H - 1}):
+        b, h = divmod(bh, H)
+        one = [t[b, h].cpu()[None, None] for t in (q, k, v)]   # per-head scales: one head is self-contained
+        ro, rl, _ = fp8.fp8_attention(*one, scale, True, signs=signs.numpy(), rows=rows)
+        o = out[b, h].float().cpu().numpy()[rows].astype(np.float64)
+        l = lse[b, h].cpu().numpy()[rows].astype(np.float64)
+        err = np.abs(o - ro.reshape(-1, d)[rows])
+        lerr = np.abs(l - rl.reshape(-1)[rows])
+        note("fp8 head %d: max|dO|=%.3e mean|dO|=%.3e max|dLSE|=%.3e" % (bh, err.max(), err.mean(), lerr.max()))
+        assert err.max() <= FP8_MAX and err.mean() <= FP8_MEAN and lerr.max() <= FP8_LSE, "fp8 head %d" % bh
