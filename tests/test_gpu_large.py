@@ -1,6 +1,6 @@
 """GPU parity beyond 2^31 elements per tensor: the dense forward, the
-split-KV decode, the backward and the FP8 forward index their tensors with
-64-bit offsets.  The tensors here
+split-KV decode, the paged decode, the backward and the FP8 forward index
+their tensors with 64-bit offsets.  The tensors here
 hold more than 2^31 elements (4 GiB and more in bf16); heads past element 2^31
 are compared with the fp64 oracle on sampled query rows (a head at a time:
 the oracle sees that head's K and V in full).
@@ -112,3 +112,44 @@ def test_fp8_past_2_31_elements(fa):
         lerr = np.abs(l - rl.reshape(-1)[rows])
         note("fp8 head %d: max|dO|=%.3e mean|dO|=%.3e max|dLSE|=%.3e" % (bh, err.max(), err.mean(), lerr.max()))
         assert err.max() <= FP8_MAX and err.mean() <= FP8_MEAN and lerr.max() <= FP8_LSE, "fp8 head %d" % bh
+
+
+def test_paged_decode_past_2_31_elements(fa):
+    # caches [num_blocks, H, 16, 128] of 33280 blocks: 2^31 + 2^25 elements each;
+    # block 32768 and above start at or past element 2^31
+    H, bs, d, B, max_len = 32, 16, 128, 4, 8192
+    per_block = H * bs * d
+    num_blocks = 2 ** 31 // per_block + 512
+    assert num_blocks * per_block > 2 ** 31
+    note("case paged B%d H%d bs%d d%d num_blocks %d (sequence 0 in blocks past element 2^31)" % (B, H, bs, d, num_blocks))
+    g = torch.Generator(device=DEV).manual_seed(4747)
+    kc = torch.empty((num_blocks, H, bs, d), dtype=torch.bfloat16, device=DEV)
+    vc = torch.empty_like(kc)
+    for t in (kc, vc):
+        for i in range(0, num_blocks, 1024):
+            t[i:i + 1024].copy_(torch.randn(t[i:i + 1024].shape, generator=g, device=DEV))
+    q = torch.randn((B, H, 1, d), generator=g, device=DEV).to(torch.bfloat16)
+    lens = torch.tensor([max_len, 8000, 5000, max_len], dtype=torch.int32)
+    max_blocks = max_len // bs
+    hg = torch.Generator().manual_seed(4747)
+    first_past = 2 ** 31 // per_block
+    table = torch.full((B, max_blocks), -1, dtype=torch.int32)
+    table[0] = first_past + torch.randperm(512, generator=hg)[:max_blocks].to(torch.int32)
+    rest = torch.randperm(first_past, generator=hg)
+    for b in range(1, B):
+        nb = -(-int(lens[b]) // bs)
+        table[b, :nb] = rest[(b - 1) * max_blocks:(b - 1) * max_blocks + nb].to(torch.int32)
+    scale = fa_inputs.default_scale(d)
+    out, lse = fa.fa_fwd_paged_decode(q, kc, vc, table.to(DEV), lens.to(DEV), 32, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    for b in (0, 2):
+        # the oracle gets the sequence's blocks, copied to the host one by one,
+        # and the table remapped onto them
+        nb = -(-int(lens[b]) // bs)
+        blocks = table[b, :nb].tolist()
+        hk = torch.stack([kc[x].cpu() for x in blocks])
+        hv = torch.stack([vc[x].cpu() for x in blocks])
+        htab = torch.arange(nb, dtype=torch.int32)[None]
+        ref_o, ref_l = oracle.paged_decode(q[b:b + 1].cpu(), hk, hv, htab, lens[b:b + 1], scale)
+        compare(out[b, :, 0].float().cpu(), lse[b].cpu(), ref_o[0], ref_l[0], "bf16", "paged sequence %d" % b)
