@@ -4,13 +4,17 @@
 
 A step is one call of the forward (``fa_fwd``; ``fa_fwd_splitkv`` for the
 decode workload; ``fa_fwd_paged_decode`` for the paged-cache decode) over one
-batch of seeded synthetic inputs already resident in device memory.  The GPU's clock ramps up over the first tens of
-milliseconds of sustained load after idle, so untimed steps run for at least
-``--prewarm-s`` seconds (0.3 by default) before the W untimed warmup steps;
-then K timed steps run back to back between two ``torch.cuda.synchronize()``
-calls.  A second pass of K steps, each between events on the stream the
-kernels run on, gives the per-launch kernel time used for the roofline
-fraction.
+batch of seeded synthetic inputs already resident in device memory.  By
+default (``--launch graph``) W untimed warm-up steps run first, then the K
+steps are captured once into a HIP graph and replayed: untimed for
+``--prewarm-s`` seconds (0.3 by default; the GPU's clock ramps up over the
+first tens of milliseconds of load after idle), then one replay between two
+``torch.cuda.synchronize()`` calls is the timed region, and the events around
+it on the kernels' stream give the per-launch kernel time used for the
+roofline fraction.  Replaying a graph keeps the host's per-call cost out of
+the timed region, which matters for kernels of a few microseconds.
+``--launch eager`` calls the K steps one by one instead (pre-warm steps,
+W warm-up steps, K timed steps, then K steps between per-step events).
 
 By default (``--workload configs``) the five configurations are timed in
 turn, one JSON line each: single-head fp32, ragged causal fp16, long
@@ -270,38 +274,93 @@ def environment():
             "rocm": rocm, "torch_hip": torch.version.hip}
 
 
+# How the timed steps are launched: "graph" (default) captures the K steps
+# once into a HIP graph on a side stream and replays it, so that the host's
+# per-call cost (argument checks, the ctypes call, the launch API) is not in
+# the timed region -- it dominates workloads whose kernels take a few us;
+# "eager" calls the K steps from Python.
+LAUNCH = "graph"
+
+
 def time_steps(step, steps, warmup, prewarm_s):
     """(ms per step over the timed region, mean per-step kernel ms from the
-    events, {median, min} of those per-step times).  The K timed steps run
-    back to back between two synchronisations; the per-step events are
-    recorded in a second pass of K steps, so that recording them adds
-    nothing to the timed region (it matters for kernels of a few us)."""
+    events, {median, min} of those per-step times).
+
+    eager: untimed steps for prewarm_s seconds (the clock ramps up over the
+    first tens of ms of load after idle), W warm-up steps, then the K timed
+    steps back to back between two synchronisations; then K more steps, each
+    between its own pair of events, give the per-step times.  graph: the W
+    warm-up steps run eagerly on a side stream (which gives that stream its
+    library workspace), the K steps are captured into one graph on it, the
+    graph is replayed untimed for prewarm_s seconds (after the GPU idled
+    during the capture), then one replay between two synchronisations (the
+    timed region) and between two events gives ms per step and the mean;
+    five more replays between events give the spread of (replay time / K)."""
     import torch
     dev = torch.device("cuda:0")
-    t_end = time.perf_counter() + prewarm_s
-    while time.perf_counter() < t_end:   # clock ramp-up: untimed
-        for _ in range(4):
-            step()
-        torch.cuda.synchronize()
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for s, e in ev:
-        s.record(stream)
-        step()
-        e.record(stream)
-    torch.cuda.synchronize()
-    t = sorted(s.elapsed_time(e) for s, e in ev)
+    if LAUNCH == "eager":
+        stream = torch.cuda.current_stream(dev)
+    else:
+        stream = torch.cuda.Stream(device=dev)   # default priority
+        stream.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(stream):
+        if LAUNCH == "eager":
+            t_end = time.perf_counter() + prewarm_s
+            while time.perf_counter() < t_end:   # clock ramp-up: untimed
+                for _ in range(4):
+                    step()
+                torch.cuda.synchronize()
+            for _ in range(warmup):
+                step()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                step()
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+            for s, e in ev:
+                s.record(stream)
+                step()
+                e.record(stream)
+            torch.cuda.synchronize()
+            t = sorted(s.elapsed_time(e) for s, e in ev)
+            mean = sum(t) / len(t)
+        else:
+            for _ in range(max(warmup, 1)):
+                step()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for _ in range(steps):
+                    step()
+            torch.cuda.synchronize()
+            t_end = time.perf_counter() + prewarm_s
+            while True:                           # clock ramp-up: untimed replays
+                g.replay()
+                torch.cuda.synchronize()
+                if time.perf_counter() >= t_end:
+                    break
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+            mean = e0.elapsed_time(e1) / steps
+            t = []
+            for _ in range(5):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                g.replay()
+                b.record(stream)
+                torch.cuda.synchronize()
+                t.append(a.elapsed_time(b) / steps)
+            t.sort()
     n = len(t)
     spread = {"kernel_ms_median": t[n // 2] if n % 2 else 0.5 * (t[n // 2 - 1] + t[n // 2]), "kernel_ms_min": t[0]}
-    return wall * 1e3 / steps, sum(t) / n, spread
+    return wall * 1e3 / steps, mean, spread
 
 
 def run_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s=0.3):
@@ -363,7 +422,7 @@ def run_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s=0.3):
     rec = {
         "metric": "attention fwd TFLOP/s (and % of MI355X bf16 MFMA/HBM roofline) per config",
         "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
-        "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, **spread, "prewarm_s": prewarm_s,
+        "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, **spread, "prewarm_s": prewarm_s, "launch": LAUNCH,
         "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "e4m3" if w.fp8 else w.dtype,
         "data": "synthetic (seeded randn, cast with RNE)",
@@ -434,7 +493,7 @@ def run_paged_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s):
     rec = {
         "metric": "attention fwd TFLOP/s (and % of MI355X bf16 MFMA/HBM roofline) per config",
         "value": flops / (ms_per_step * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
-        "warmup": warmup, "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, **spread, "prewarm_s": prewarm_s,
+        "warmup": warmup, "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, **spread, "prewarm_s": prewarm_s, "launch": LAUNCH,
         "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded randn, shuffled block table)",
         "config": {"workload": name, "B": w.B, "H": w.H, "d": w.d, "block_size": w.block_size,
@@ -487,7 +546,7 @@ def run_varlen_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s):
     rec = {
         "metric": "attention fwd TFLOP/s (and % of MI355X bf16 MFMA/HBM roofline) per config",
         "value": flops / (ms_per_step * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
-        "warmup": warmup, "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, **spread, "prewarm_s": prewarm_s,
+        "warmup": warmup, "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, **spread, "prewarm_s": prewarm_s, "launch": LAUNCH,
         "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded randn, seeded length mix)",
         "config": {"workload": name, "S": w.S, "H": w.H, "d": w.d, "causal": w.causal, "dtype": w.dtype,
@@ -738,6 +797,9 @@ def main():
                     help="target oracle time for each line's cpu_baseline")
     ap.add_argument("--prewarm-s", type=float, default=0.3,
                     help="seconds of untimed steps before the warmup steps (lets the GPU clock ramp up)")
+    ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
+                    help="graph: capture the K timed steps into a HIP graph and replay it (default); eager: call them "
+                         "one by one from Python")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of attention, run --steps plain device-to-device copies of this many bytes "
                          "(the reference kernel for calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -750,6 +812,8 @@ def main():
     ap.add_argument("--print-profile-commands", metavar="DIR", default=None,
                     help="print the rocprofv3 commands whose output --summarize-rocprof DIR reads")
     args = ap.parse_args()
+    global LAUNCH
+    LAUNCH = args.launch
     if args.summarize_rocprof:
         return summarize_rocprof(args.summarize_rocprof, args.workload, os.path.join(ROOT, "profiles"),
                                  kernel=args.kernel)
