@@ -284,7 +284,7 @@ LAUNCH = "graph"
 
 def time_steps(step, steps, warmup, prewarm_s):
     """(ms per step over the timed region, mean per-step kernel ms from the
-    events, {median, min} of those per-step times).
+    events, {median, min} of those per-step times, the launch mode used).
 
     eager: untimed steps for prewarm_s seconds (the clock ramps up over the
     first tens of ms of load after idle), W warm-up steps, then the K timed
@@ -298,13 +298,26 @@ def time_steps(step, steps, warmup, prewarm_s):
     five more replays between events give the spread of (replay time / K)."""
     import torch
     dev = torch.device("cuda:0")
-    if LAUNCH == "eager":
+    launch = LAUNCH
+    if launch == "graph":
+        try:
+            return _time_steps(step, steps, warmup, prewarm_s, "graph") + ("graph",)
+        except RuntimeError as e:   # capture refused: time the same steps eagerly instead
+            print("bench: graph capture failed (%s); timing eager calls" % e, file=sys.stderr, flush=True)
+            torch.cuda.synchronize()
+    return _time_steps(step, steps, warmup, prewarm_s, "eager") + ("eager",)
+
+
+def _time_steps(step, steps, warmup, prewarm_s, launch):
+    import torch
+    dev = torch.device("cuda:0")
+    if launch == "eager":
         stream = torch.cuda.current_stream(dev)
     else:
         stream = torch.cuda.Stream(device=dev)   # default priority
         stream.wait_stream(torch.cuda.current_stream(dev))
     with torch.cuda.stream(stream):
-        if LAUNCH == "eager":
+        if launch == "eager":
             t_end = time.perf_counter() + prewarm_s
             while time.perf_counter() < t_end:   # clock ramp-up: untimed
                 for _ in range(4):
@@ -382,7 +395,7 @@ def run_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s=0.3):
     if w.fp8:
         signs = fa_inputs.make_signs(w.d, w.seed).to(dev)
         pack = fa.fa_quantize_fp8(qd, kd, vd, signs=signs)
-        qms, _, _ = time_steps(lambda: fa.fa_quantize_fp8(qd, kd, vd, signs=signs, pack=pack), 5, 1, 0.0)
+        qms, _, _, _ = time_steps(lambda: fa.fa_quantize_fp8(qd, kd, vd, signs=signs, pack=pack), 5, 1, 0.0)
         extra["quantize_ms"] = qms
 
         def step():
@@ -405,7 +418,7 @@ def run_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s=0.3):
         def step():
             fa.fa_fwd(qd, kd, vd, scale=w.scale, causal=w.causal, out=out, lse=lse)
 
-    ms_per_step, kernel_ms, spread = time_steps(step, steps, warmup, prewarm_s)
+    ms_per_step, kernel_ms, spread, launch = time_steps(step, steps, warmup, prewarm_s)
     flops = workload_flops(w)
     nbytes = workload_bytes(w)
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -422,7 +435,7 @@ def run_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s=0.3):
     rec = {
         "metric": "attention fwd TFLOP/s (and % of MI355X bf16 MFMA/HBM roofline) per config",
         "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
-        "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, **spread, "prewarm_s": prewarm_s, "launch": LAUNCH,
+        "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, **spread, "prewarm_s": prewarm_s, "launch": launch,
         "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "e4m3" if w.fp8 else w.dtype,
         "data": "synthetic (seeded randn, cast with RNE)",
@@ -483,7 +496,7 @@ def run_paged_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s):
     def step():
         fa.fa_fwd_paged_decode(qd, kcd, vcd, td, ld, w.num_splits, scale=w.scale, workspace=ws, out=out, lse=lse)
 
-    ms_per_step, kernel_ms, spread = time_steps(step, steps, warmup, prewarm_s)
+    ms_per_step, kernel_ms, spread, launch = time_steps(step, steps, warmup, prewarm_s)
     keys = int(lens.clamp(min=0).sum())
     flops = 4.0 * w.H * w.d * keys
     nbytes = paged_bytes(w, lens.tolist(), table.numel())
@@ -493,7 +506,7 @@ def run_paged_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s):
     rec = {
         "metric": "attention fwd TFLOP/s (and % of MI355X bf16 MFMA/HBM roofline) per config",
         "value": flops / (ms_per_step * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
-        "warmup": warmup, "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, **spread, "prewarm_s": prewarm_s, "launch": LAUNCH,
+        "warmup": warmup, "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, **spread, "prewarm_s": prewarm_s, "launch": launch,
         "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded randn, shuffled block table)",
         "config": {"workload": name, "B": w.B, "H": w.H, "d": w.d, "block_size": w.block_size,
@@ -537,7 +550,7 @@ def run_varlen_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s):
     def step():
         fa.fa_fwd_varlen(qd, kd, vd, cqd, ckd, scale=w.scale, causal=w.causal, out=out, lse=lse, workspace=ws)
 
-    ms_per_step, kernel_ms, spread = time_steps(step, steps, warmup, prewarm_s)
+    ms_per_step, kernel_ms, spread, launch = time_steps(step, steps, warmup, prewarm_s)
     lq = (cq[1:] - cq[:-1]).tolist()
     lk = (ck[1:] - ck[:-1]).tolist()
     flops = 4.0 * w.d * w.H * varlen_pairs(w, lq, lk)
@@ -546,7 +559,7 @@ def run_varlen_workload(name, steps, warmup, with_cpu, cpu_target_s, prewarm_s):
     rec = {
         "metric": "attention fwd TFLOP/s (and % of MI355X bf16 MFMA/HBM roofline) per config",
         "value": flops / (ms_per_step * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
-        "warmup": warmup, "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, **spread, "prewarm_s": prewarm_s, "launch": LAUNCH,
+        "warmup": warmup, "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, **spread, "prewarm_s": prewarm_s, "launch": launch,
         "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded randn, seeded length mix)",
         "config": {"workload": name, "S": w.S, "H": w.H, "d": w.d, "causal": w.causal, "dtype": w.dtype,
