@@ -160,21 +160,31 @@ void bwd_dq_kernel(BwdArgs a) {
         }
     };
 
+    const int kv_end = CAUSAL ? min(Nk, q0 + BR) : Nk;
+    const int nt = (kv_end + BC - 1) / BC;
+    // the first tile's copy goes out before the row loads, so that they wait
+    // on memory together
+    issue_tile(0, 0);
+
     // Q and dO fragments (B operands): lane (query l32, half g) holds dims
     // [16*ks + 8*g, +8); the same dims of O give the lane's half of D.
+    // Every lane loads (rows past the end read the last row, then are
+    // zeroed): no branches around the loads.
     const int row = q0w + l32;
-    const bool row_ok = row < Nq;
+    const bool row_ok = row < Nq;  // Nq >= 1
+    const size_t rbase = qbase + (size_t)(row_ok ? row : Nq - 1) * D;
     x8 qf[KS], dof[KS];
     float dpart = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        u32x4 rq = {0u, 0u, 0u, 0u}, rdo = {0u, 0u, 0u, 0u}, ro = {0u, 0u, 0u, 0u};
-        if (row_ok) {
-            const size_t off = qbase + (size_t)row * D + 16 * ks + 8 * g;
-            rq = *reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.q) + off);
-            rdo = *reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.dout) + off);
-            ro = *reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.out) + off);
-        }
+        const size_t off = rbase + 16 * ks + 8 * g;
+        u32x4 rq = *reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.q) + off);
+        u32x4 rdo = *reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.dout) + off);
+        u32x4 ro = *reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.out) + off);
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        rq = row_ok ? rq : zero;
+        rdo = row_ok ? rdo : zero;
+        ro = row_ok ? ro : zero;
         qf[ks] = __builtin_bit_cast(x8, (rq ^ a.sflip) & a.skeep);  // the scale's sign, folded into Q
         dof[ks] = __builtin_bit_cast(x8, rdo);
         const x8 of = __builtin_bit_cast(x8, ro);
@@ -193,9 +203,6 @@ void bwd_dq_kernel(BwdArgs a) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.0f;
-
-    const int kv_end = CAUSAL ? min(Nk, q0 + BR) : Nk;
-    const int nt = (kv_end + BC - 1) / BC;
 
     auto compute_tile = [&](auto stage_tag, int k0) {
         constexpr int S = decltype(stage_tag)::value;
@@ -298,8 +305,7 @@ void bwd_dq_kernel(BwdArgs a) {
         __syncthreads();
     };
 
-    issue_tile(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the first tile (issued above) has landed
     __syncthreads();
     for (int jt = 0; jt < nt; jt += 2) {
         step(Int<0>{}, jt);
@@ -427,6 +433,34 @@ void bwd_dkdv_kernel(BwdArgs a) {
         }
     };
 
+    auto issue_v_rows = [&]() {
+        // the workgroup's BK V rows, K-style swizzle (read row-wise only);
+        // rows past the end repeat the last key
+        const T *vhead = static_cast<const T *>(a.v) + (size_t)bh * Nk * D;
+        const __amdgpu_buffer_rsrc_t rsrc_v = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<T *>(vhead), (short)0, (int)((uint32_t)Nk * ROW), kBufferDword3);
+#pragma unroll
+        for (int n = 0; n < VUNITS / NT; ++n) {
+            const int u = (n * NW + wave) * 64 + lane;
+            uint32_t o = (uint32_t)layout::k_dma_src_elem<D>(u) * 2;
+            const int over = k0 + u / CH - (Nk - 1);
+            if (over > 0) o -= (uint32_t)over * ROW;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_v, (FA_LDS void *)(smem + VT_OFF + (n * NW + wave) * 1024),
+                                                     16, o, (uint32_t)k0 * ROW, 0, 0);
+        }
+    };
+
+    // query tiles: under the mask only queries >= k0 see a key of the block
+    const int q_begin = CAUSAL ? (k0 / BQ) * BQ : 0;
+    const int nt = q_begin < Nq ? (Nq - q_begin + BQ - 1) / BQ : 0;
+    // the V rows and the first query tile go out before the K and V
+    // fragment loads, so that they all wait on memory together
+    if (nt > 0) {  // workgroup-uniform
+        if constexpr (VLDS) issue_v_rows();
+        issue_tile(q_begin, 0);
+    }
+
+
     // K and V fragments (B operands of S = Q K^T and dP = dO V^T): lane (key
     // l32, half g) holds dims [16*ks + 8*g, +8).  Keys past the end repeat
     // the last key; their gradients are not stored.
@@ -455,27 +489,6 @@ void bwd_dkdv_kernel(BwdArgs a) {
             dkacc[db][r] = 0.0f;
             dvacc[db][r] = 0.0f;
         }
-
-    auto issue_v_rows = [&]() {
-        // the workgroup's BK V rows, K-style swizzle (read row-wise only);
-        // rows past the end repeat the last key
-        const T *vhead = static_cast<const T *>(a.v) + (size_t)bh * Nk * D;
-        const __amdgpu_buffer_rsrc_t rsrc_v = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<T *>(vhead), (short)0, (int)((uint32_t)Nk * ROW), kBufferDword3);
-#pragma unroll
-        for (int n = 0; n < VUNITS / NT; ++n) {
-            const int u = (n * NW + wave) * 64 + lane;
-            uint32_t o = (uint32_t)layout::k_dma_src_elem<D>(u) * 2;
-            const int over = k0 + u / CH - (Nk - 1);
-            if (over > 0) o -= (uint32_t)over * ROW;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_v, (FA_LDS void *)(smem + VT_OFF + (n * NW + wave) * 1024),
-                                                     16, o, (uint32_t)k0 * ROW, 0, 0);
-        }
-    };
-
-    // query tiles: under the mask only queries >= k0 see a key of the block
-    const int q_begin = CAUSAL ? (k0 / BQ) * BQ : 0;
-    const int nt = q_begin < Nq ? (Nq - q_begin + BQ - 1) / BQ : 0;
 
     auto compute_tile = [&](auto stage_tag, int qt) {
         constexpr int S = decltype(stage_tag)::value;
@@ -579,9 +592,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
         __syncthreads();
     };
 
-    if (nt > 0) {
-        if constexpr (VLDS) issue_v_rows();
-        issue_tile(q_begin, 0);
+    if (nt > 0) {  // the V rows and the first tile (issued above) have landed
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         for (int jt = 0; jt < nt; jt += 2) {

@@ -482,18 +482,25 @@ void fp8_fwd_kernel(Fp8Args a) {
             voff[db][h] = KTILE + dim * VROW + ((ch ^ tile_swz<VROW>(dim)) * 16);
         }
 
+    const int kv_end = CAUSAL ? min(Nk, q0 + BR) : Nk;
+    const int nt = (kv_end + BC - 1) / BC;
+    // the first tile's copy goes out before the Q loads, so that the two
+    // wait on memory together
+    if (nt > 0) issue_tile(0, 0);
+
     // Q code fragments (B operand of S^T): lane (query l32, half g) holds
-    // dims [64*ks + 32*g, +32)
+    // dims [64*ks + 32*g, +32).  Every lane loads (rows past the end read
+    // the last row, then are zeroed): no branches around the loads.
     const int row = q0w + l32;
+    const bool row_ok = row < Nq;  // Nq >= 1
+    const uint8_t *qrow = a.q8 + ((size_t)bh * Nq + (row_ok ? row : Nq - 1)) * D;
     i32x8 qf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
-        if (row < Nq) {
-            const uint8_t *p = a.q8 + ((size_t)bh * Nq + row) * D + 64 * ks + 32 * g;
-            lo = *reinterpret_cast<const u32x4 *>(p);
-            hi = *reinterpret_cast<const u32x4 *>(p + 16);
-        }
+        u32x4 lo = *reinterpret_cast<const u32x4 *>(qrow + 64 * ks + 32 * g);
+        u32x4 hi = *reinterpret_cast<const u32x4 *>(qrow + 64 * ks + 32 * g + 16);
+        lo = row_ok ? lo : u32x4{0u, 0u, 0u, 0u};
+        hi = row_ok ? hi : u32x4{0u, 0u, 0u, 0u};
         lo = (lo ^ a.qflip) & a.qkeep;  // the sign of the scale, folded into Q
         hi = (hi ^ a.qflip) & a.qkeep;
         qf[ks] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -523,9 +530,6 @@ void fp8_fwd_kernel(Fp8Args a) {
 #pragma unroll
         for (int w = 0; w < 8; ++w) ones8[w] = ones;
     }
-
-    const int kv_end = CAUSAL ? min(Nk, q0 + BR) : Nk;
-    const int nt = (kv_end + BC - 1) / BC;
 
     auto compute_tile = [&](auto stage_tag, int k0) {
         constexpr int S = decltype(stage_tag)::value;
@@ -623,8 +627,7 @@ void fp8_fwd_kernel(Fp8Args a) {
         __syncthreads();
     };
 
-    if (nt > 0) {
-        issue_tile(0, 0);
+    if (nt > 0) {  // the first tile's copy (issued above) has landed for every thread
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }

@@ -241,16 +241,30 @@ void prefill_kernel(PrefillArgs a) {
         }
     };
 
+    const int kv_end = CAUSAL ? min(Nk, q0 + BR) : Nk;
+    // keys [kbeg, kend) of this workgroup: all visible ones, or one chunk
+    const int kbeg = SPLIT ? min(kv_end, chunk_idx * a.chunk) : 0;
+    const int kend = SPLIT ? min(kv_end, kbeg + a.chunk) : kv_end;
+    const int nt = (kend - kbeg + BCS - 1) / BCS;  // steps
+    // The first step's K/V copy goes out before the Q loads, so that the two
+    // wait on memory together (workgroup-uniform; a sequence or chunk
+    // without keys has no step).
+    if (nt > 0) issue_tile(kbeg, 0);
+
     // Q fragments (B operand of S^T): lane (query l32 of block qb, half g)
-    // holds dims [16*ks + 8*g, +8).
+    // holds dims [16*ks + 8*g, +8).  Every lane loads (rows past the end
+    // read the last row, then are zeroed), so the loads carry no branches
+    // and all go out before any of them is waited for.
     x8 qf[QB][KS];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int row = q0w + 32 * qb + l32;
+        const bool row_ok = row < Nq;  // a workgroup exists only for Nq >= 1
+        const T *qrow = qp + (size_t)(row_ok ? row : Nq - 1) * RS;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            u32x4 raw = {0u, 0u, 0u, 0u};
-            if (row < Nq) raw = *reinterpret_cast<const u32x4 *>(qp + (size_t)row * RS + 16 * ks + 8 * g);
+            u32x4 raw = *reinterpret_cast<const u32x4 *>(qrow + 16 * ks + 8 * g);
+            raw = row_ok ? raw : u32x4{0u, 0u, 0u, 0u};
             raw = (raw ^ a.qflip) & a.qkeep;  // the sign of the scale, folded into Q
             qf[qb][ks] = __builtin_bit_cast(x8, raw);
         }
@@ -289,12 +303,6 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.0f;
     }
-
-    const int kv_end = CAUSAL ? min(Nk, q0 + BR) : Nk;
-    // keys [kbeg, kend) of this workgroup: all visible ones, or one chunk
-    const int kbeg = SPLIT ? min(kv_end, chunk_idx * a.chunk) : 0;
-    const int kend = SPLIT ? min(kv_end, kbeg + a.chunk) : kv_end;
-    const int nt = (kend - kbeg + BCS - 1) / BCS;  // steps
 
     auto compute_tile = [&](auto stage_tag, int k0) {
         constexpr int S = decltype(stage_tag)::value;
@@ -481,8 +489,7 @@ void prefill_kernel(PrefillArgs a) {
         __syncthreads();                                    // ... and every thread's; stage S is free
     };
 
-    if (nt > 0) {  // workgroup-uniform; a sequence (or chunk) without keys has no tile
-        issue_tile(kbeg, 0);
+    if (nt > 0) {  // the first step's copy (issued above) has landed for every thread
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
