@@ -61,6 +61,12 @@
  * on the host before any HIP call, so a rejected call has no device side
  * effects.  ``fa_last_error`` returns a message for the calling thread's
  * most recent failure.
+ *
+ * Index range.  B*H, Nq*d and Nk*d must each fit in 31 bits (one head's
+ * rows are addressed with 32-bit byte offsets), and B*H*max(Nq, Nk)*d may
+ * not exceed 2^48 elements (far past any device's memory; it keeps every
+ * byte count in 64 bits); larger calls return FA_ERR_UNSUPPORTED.  Whole
+ * tensors may exceed 2^31 elements: they are indexed with 64-bit offsets.
  */
 #ifndef IO_AWARE_AMD_FA_H
 #define IO_AWARE_AMD_FA_H

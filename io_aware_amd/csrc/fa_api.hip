@@ -62,6 +62,10 @@ int check_common(const void *q, const void *k, const void *v, const void *out, c
     if (d != 32 && d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "d must be 32, 64 or 128");
     if ((int64_t)B * H > INT32_MAX || (int64_t)Nq * d > INT32_MAX || (int64_t)Nk * d > INT32_MAX)
         return fail(FA_ERR_UNSUPPORTED, "B*H, Nq*d and Nk*d must each fit in 31 bits");
+    // every byte count below (tensors, split workspaces of up to 1024 chunks)
+    // then stays far inside 64 bits; 2^48 elements is beyond any device
+    if ((int64_t)B * H * ((int64_t)(Nq > Nk ? Nq : Nk) * d) > ((int64_t)1 << 48))
+        return fail(FA_ERR_UNSUPPORTED, "B*H*N*d must not exceed 2^48 elements");
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
         return fail(FA_ERR_UNSUPPORTED, "q, k, v and out must be 16-byte aligned");
     if (lse && !aligned(lse, 4)) return fail(FA_ERR_UNSUPPORTED, "lse must be 4-byte aligned");

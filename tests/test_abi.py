@@ -86,6 +86,7 @@ def call_fwd(fa, **over):
     (dict(d=48), 2), (dict(d=256), 2), (dict(d=16), 2),
     (dict(q=Q + 8), 2), (dict(out=O + 4), 2), (dict(lse=L + 2), 2),
     (dict(Nq=1 << 26, d=64), 2),
+    (dict(B=1 << 15, H=1 << 15, Nq=1 << 20, Nk=1 << 20, d=64), 2),   # 2^56 elements: past the 2^48 cap
     (dict(out=Q + 64), 1), (dict(lse=K + 1024), 1), (dict(lse=O + 16), 1),
 ])
 def test_fwd_rejects_invalid_arguments(fa, over, code):
