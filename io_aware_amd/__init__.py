@@ -140,9 +140,31 @@ def _shapes(q, k, v):
     return B, H, Nq, Nk, d
 
 
+def _expect(t, name, shape, dtype, device):
+    """A caller-supplied output or buffer: the library writes (or reads)
+    exactly ``shape`` elements of ``dtype`` through its pointer, so it must
+    be a contiguous tensor of that shape and type on ``device``."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous %s tensor of shape %s on %s (got %s %s on %s)"
+                         % (name, dtype, tuple(shape), device, t.dtype, tuple(t.shape), t.device))
+
+
+def _buffer(t, name, need, device):
+    """A caller-supplied byte buffer (workspace, pack) of at least ``need``
+    bytes on ``device``."""
+    if t is None:
+        return
+    if t.device != device or not t.is_contiguous() or t.numel() * t.element_size() < need:
+        raise ValueError("%s must be a contiguous tensor of at least %d bytes on %s" % (name, need, device))
+
+
 def _outputs(q, out, lse, want_lse):
     import torch
     B, H, Nq, d = q.shape
+    _expect(out, "out", q.shape, q.dtype, q.device)
+    _expect(lse, "lse", (B, H, Nq), torch.float32, q.device)
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
@@ -171,9 +193,12 @@ def fa_fwd_noalloc(q, k, v, out, lse=None, scale=None, causal=False, stream=None
     """fa_fwd through the entry point that allocates no device memory (its
     split workspace is the library's static scratch array).  ``out`` (and
     ``lse``, if wanted) must be given.  Returns (out, lse)."""
+    import torch
     B, H, Nq, Nk, d = _shapes(q, k, v)
     if out is None:
         raise ValueError("fa_fwd_noalloc writes into caller-owned outputs: pass out")
+    _expect(out, "out", q.shape, q.dtype, q.device)
+    _expect(lse, "lse", (B, H, Nq), torch.float32, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     _check(lib.fa_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d, float(scale),
@@ -196,6 +221,7 @@ def fa_fwd_splitkv(q, k, v, num_splits, scale=None, workspace=None, out=None, ls
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = fa_splitkv_workspace_bytes(B, H, Nq, d, num_splits)
+    _buffer(workspace, "workspace", 0, q.device)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
@@ -226,6 +252,8 @@ def fa_fwd_paged_decode(q, k_cache, v_cache, block_table, seq_lens, num_splits, 
                     ("seq_lens", seq_lens)):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("%s must be a contiguous device tensor" % name)
+    _expect(out, "out", q.shape, q.dtype, q.device)
+    _expect(lse, "lse", (B, H), torch.float32, q.device)
     if out is None:
         out = torch.empty_like(q)
     if lse is None and return_lse:
@@ -233,6 +261,7 @@ def fa_fwd_paged_decode(q, k_cache, v_cache, block_table, seq_lens, num_splits, 
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = fa_splitkv_workspace_bytes(B, H, 1, d, num_splits)
+    _buffer(workspace, "workspace", 0, q.device)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
@@ -264,12 +293,15 @@ def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale=None, causal=False,
             cu_seqlens_q.dim() != 1 or cu_seqlens_q.shape != cu_seqlens_k.shape:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must be int32 [S + 1]")
     S = cu_seqlens_q.shape[0] - 1
+    _expect(out, "out", q.shape, q.dtype, q.device)
+    _expect(lse, "lse", (H, total_q), torch.float32, q.device)
     out = torch.empty_like(q) if out is None else out
     if lse is None and return_lse:
         lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = fa_varlen_workspace_bytes(S, total_q)
+    _buffer(workspace, "workspace", 0, q.device)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
@@ -290,6 +322,7 @@ def fa_quantize_fp8(q, k, v, signs=None, pack=None, stream=None):
     import torch
     B, H, Nq, Nk, d = _shapes(q, k, v)
     need = fa_fp8_pack_bytes(B, H, Nq, Nk, d)
+    _buffer(pack, "pack", 0, q.device)
     if pack is None:
         pack = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     if signs is not None and (signs.dtype != torch.float32 or signs.numel() != d or not signs.is_cuda):
@@ -303,6 +336,13 @@ def fa_fwd_fp8(pack, B, H, Nq, Nk, d, scale=None, causal=False, out_dtype=None, 
                return_lse=True, stream=None):
     """Attention on an E4M3 pack.  Returns (out [B, H, Nq, d], lse [B, H, Nq])."""
     import torch
+    # the pack is read whole: it must hold what fa_quantize_fp8 wrote for these sizes
+    _buffer(pack, "pack", fa_fp8_pack_bytes(B, H, Nq, Nk, d), pack.device)
+    if not pack.is_cuda:
+        raise ValueError("pack must be a device tensor")
+    if out is not None:
+        _expect(out, "out", (B, H, Nq, d), out.dtype, pack.device)
+    _expect(lse, "lse", (B, H, Nq), torch.float32, pack.device)
     if out is None:
         out = torch.empty((B, H, Nq, d), dtype=out_dtype or torch.bfloat16, device=pack.device)
     if lse is None and return_lse:
@@ -329,14 +369,17 @@ def fa_bwd(q, k, v, out, dout, lse, scale=None, causal=False, dq=None, dk=None, 
     for name, t in (("out", out), ("dout", dout)):
         if tuple(t.shape) != tuple(q.shape) or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
             raise ValueError("%s must be a contiguous device tensor shaped and typed like q" % name)
-    if tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    _expect(lse, "lse", (B, H, Nq), torch.float32, q.device)
+    _expect(dq, "dq", q.shape, q.dtype, q.device)
+    _expect(dk, "dk", k.shape, k.dtype, k.device)
+    _expect(dv, "dv", v.shape, v.dtype, v.device)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = fa_bwd_workspace_bytes(B, H, Nq, d)
+    _buffer(workspace, "workspace", 0, q.device)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()

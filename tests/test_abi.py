@@ -414,3 +414,26 @@ def test_fp8_pack_bytes_follow_the_documented_layout(fa):
     assert fa.fa_fp8_pack_bytes(B, H, Nq, Nk, d) == want
     assert fa.fa_fp8_pack_bytes(B, H, Nq, Nk, 32) == 0
     assert call_quant(fa, pack_bytes=want - 1) == 4
+
+
+def test_binding_checks_caller_outputs(fa):
+    # the library writes through an output pointer without knowing its size:
+    # the binding accepts only a contiguous tensor of the exact shape and type
+    import torch
+    cpu = torch.device("cpu")
+    good = torch.empty((2, 3, 5), dtype=torch.float32)
+    fa._expect(good, "lse", (2, 3, 5), torch.float32, cpu)
+    fa._expect(None, "lse", (2, 3, 5), torch.float32, cpu)
+    for bad in (torch.empty((2, 3, 4), dtype=torch.float32),             # too small
+                torch.empty((2, 3, 6), dtype=torch.float32),             # wrong shape
+                torch.empty((2, 3, 5), dtype=torch.float16),             # wrong type
+                torch.empty((2, 5, 3), dtype=torch.float32).transpose(1, 2)):   # strided
+        with pytest.raises(ValueError):
+            fa._expect(bad, "lse", (2, 3, 5), torch.float32, cpu)
+    with pytest.raises(ValueError):
+        fa._expect(good, "lse", (2, 3, 5), torch.float32, torch.device("cuda", 0))
+    fa._buffer(torch.empty(64, dtype=torch.uint8), "workspace", 64, cpu)
+    with pytest.raises(ValueError):
+        fa._buffer(torch.empty(63, dtype=torch.uint8), "workspace", 64, cpu)
+    with pytest.raises(ValueError):
+        fa._buffer(torch.empty(64, dtype=torch.uint8), "workspace", 0, torch.device("cuda", 0))

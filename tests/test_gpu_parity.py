@@ -431,6 +431,31 @@ def test_lse_optional(fa):
     assert torch.equal(o1, o2)
 
 
+def test_binding_rejects_mismatched_outputs(fa):
+    """An output of the wrong size, type or layout is refused before any
+    launch (the library cannot see buffer sizes), and the refused tensors are
+    left as they were."""
+    q, k, v = fa_inputs.make_qkv(1, 2, 100, 80, 64, "bf16", seed=27)
+    qd, kd, vd = to_dev(q, k, v)
+    out, lse = fa.fa_fwd(qd, kd, vd)
+    g = torch.randn_like(qd)
+    small = torch.full((1, 2, 99, 64), 3.0, dtype=torch.bfloat16, device=DEV)
+    cases = [
+        lambda: fa.fa_fwd(qd, kd, vd, out=small),
+        lambda: fa.fa_fwd(qd, kd, vd, out=torch.empty_like(qd, dtype=torch.float16)),
+        lambda: fa.fa_fwd(qd, kd, vd, lse=torch.empty((1, 2, 100), dtype=torch.float16, device=DEV)),
+        lambda: fa.fa_fwd_noalloc(qd, kd, vd, torch.empty((1, 100, 2, 64), dtype=torch.bfloat16,
+                                                          device=DEV).transpose(1, 2)),
+        lambda: fa.fa_bwd(qd, kd, vd, out, g, lse, dk=torch.empty_like(qd)),
+        lambda: fa.fa_bwd(qd, kd, vd, out, g, lse, workspace=torch.empty(1 << 20, dtype=torch.uint8)),
+    ]
+    for call in cases:
+        with pytest.raises(ValueError):
+            call()
+    torch.cuda.synchronize()
+    assert (small.float() == 3.0).all()
+
+
 def test_large_values_and_rising_scores_stay_finite(fa):
     """bf16 values near 2^94 with scores that climb slowly along 16384 keys:
     the lazy rescale bounds the running sum of P (not each tile's), so the
