@@ -130,7 +130,9 @@ typedef enum fa_status {
  *    memory, with no workspace.
  * The environment variable FA_PREFILL_SPLIT overrides the first choice: 0
  * or 1 never splits, n >= 2 asks for n chunks (capped at the tile count);
- * FA_PREFILL_SHAPE forces a tile shape (sweeps).
+ * FA_PREFILL_SHAPE forces a tile shape (sweeps); FA_PREFILL_PIPE=1 runs the
+ * 32-key-tile shape with a pipelined schedule (same results bit for bit,
+ * slower on this GPU; for measurement).
  * float32 runs the vector-ALU kernel over (batch*head, Q block of 64)
  * workgroups; a grid of fewer than 256 cuts each Q block's key range into
  * min(ceil(512 / grid), 64) chunks of whole 32-key blocks (fewer where

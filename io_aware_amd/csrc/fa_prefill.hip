@@ -35,7 +35,10 @@
 //    taken before scaling.
 //  * Each wave raises its priority (s_setprio) while it issues the S^T
 //    MFMA chain and drops it for the softmax and P V, which keeps the
-//    co-resident waves of a SIMD in different phases.
+//    co-resident waves of a SIMD in different phases.  (A pipelined schedule
+//    that overlaps inside each wave instead, the next tile's S^T chain
+//    interleaved with this tile's softmax as FlashAttention-3 overlaps
+//    GEMM and softmax, is kept for measurement: FA_PREFILL_PIPE=1.)
 //  * Lazy rescale: P is formed against the max the row is held at; the
 //    accumulator is rescaled (and the held max moved to the exact running
 //    max) only when some lane's sum of P exceeds the bound: 2^15 over the
@@ -114,7 +117,8 @@ template <typename T>
 constexpr bool running_sum_bound() { return !__is_same(T, _Float16); }
 constexpr float kLn2 = 0.693147180559945309417f;
 
-template <typename T, int D, bool CAUSAL, int NW, int QW, int BC, int OCC, int MODE, int KSPLIT = 1>
+template <typename T, int D, bool CAUSAL, int NW, int QW, int BC, int OCC, int MODE, int KSPLIT = 1,
+          bool PIPE = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC)))
 void prefill_kernel(PrefillArgs a) {
     constexpr bool VARLEN = MODE == kModeVarlen;
@@ -250,6 +254,25 @@ void prefill_kernel(PrefillArgs a) {
     // wait on memory together (workgroup-uniform; a sequence or chunk
     // without keys has no step).
     if (nt > 0) issue_tile(kbeg, 0);
+    // one K or V tile of BC keys (pipelined schedule: K runs one tile ahead of V)
+    auto issue_part = [&](bool is_v, int k0, int stage) {
+        char *dbase = smem + stage * STAGE_BYTES + (is_v ? TILE_BYTES : 0);
+        const uint32_t soff = (uint32_t)k0 * RSB;
+        const bool tail = k0 + BCS > Nk;  // workgroup-uniform
+#pragma unroll
+        for (int n = 0; n < NDMA; ++n) {
+            uint32_t o = is_v ? vdma[n] : kdma[n];
+            if (tail) {
+                const int over = k0 + dkey[n] - (Nk - 1);
+                if (over > 0) o -= (uint32_t)over * RSB;
+            }
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(is_v ? rsrc_v : rsrc_k,
+                                                     (FA_LDS void *)(dbase + (n * NW + wave) * 1024), 16, o, soff, 0, 0);
+        }
+    };
+    if constexpr (PIPE) {
+        if (nt > 1) issue_part(false, kbeg + BC, 1);
+    }
 
     // Q fragments (B operand of S^T): lane (query l32 of block qb, half g)
     // holds dims [16*ks + 8*g, +8).  Every lane loads (rows past the end
@@ -489,13 +512,156 @@ void prefill_kernel(PrefillArgs a) {
         __syncthreads();                                    // ... and every thread's; stage S is free
     };
 
-    if (nt > 0) {  // the first step's copy (issued above) has landed for every thread
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-    }
-    for (int jt = 0; jt < nt; jt += 2) {
-        step(Int<0>{}, jt);
-        if (jt + 1 < nt) step(Int<1>{}, jt + 1);
+    if constexpr (!PIPE) {
+        if (nt > 0) {  // the first step's copy (issued above) has landed for every thread
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
+        for (int jt = 0; jt < nt; jt += 2) {
+            step(Int<0>{}, jt);
+            if (jt + 1 < nt) step(Int<1>{}, jt + 1);
+        }
+    } else {
+        // ---- pipelined schedule: tile j+1's S^T chain beside tile j's softmax --
+        // Step j computes S^T of tile j+1 (K in stage (j+1) & 1) while it forms
+        // P of tile j, then P V of tile j (V in stage j & 1).  K is copied two
+        // tiles ahead and V one: step j issues K of tile j+2 into stage j & 1
+        // (last read by step j-1) and V of tile j+1 into stage (j+1) & 1 (last
+        // read by step j-1), after the barrier that ends step j-1.  Per element
+        // the arithmetic and its order are those of the schedule above.
+        static_assert(QB == 1 && KB == 1 && KS2 == 2 && KSPLIT == 1, "pipelined schedule: one 32x32 tile per wave");
+        constexpr int NK = KS;
+        constexpr int KPF = NK < 3 ? NK : 3;
+        auto active_at = [&](int j) {
+            return j < nt && q0w < Nq && (!CAUSAL || kbeg + j * BC <= q0w + QW - 1);
+        };
+        // S^T of the tile in the K stage of kstage_tag into s, each MFMA
+        // followed by one K read and NVALU vector instructions of whatever
+        // the caller placed in the same block
+        auto s_chain = [&](auto kstage_tag, f32x16 &s, auto nvalu_tag) {
+            constexpr int KOFF = decltype(kstage_tag)::value * STAGE_BYTES;
+            constexpr int NVALU = decltype(nvalu_tag)::value;
+            auto read_k = [&](int i) {
+                return __builtin_bit_cast(x8, *reinterpret_cast<const u32x4 *>(smem + KOFF + koff[i]));
+            };
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+            x8 kq[KPF];
+#pragma unroll
+            for (int i = 0; i < KPF; ++i) kq[i] = read_k(i);
+#pragma unroll
+            for (int i = 0; i < NK; ++i) {
+                const x8 kf = kq[i % KPF];
+                if (i + KPF < NK) kq[i % KPF] = read_k(i + KPF);
+                s = M::run(kf, qf[0][i], s);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, KPF, 0);
+#pragma unroll
+            for (int i = 0; i < NK; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (i + KPF < NK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if constexpr (NVALU > 0) __builtin_amdgcn_sched_group_barrier(0x002, NVALU, 0);
+            }
+        };
+        auto exp_half = [&](const f32x16 &s, int h, float msub, float &lsum, x8 &p) {
+            f32x8 t;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                t[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * h + e], c, -msub));
+                lsum = (h == 0 && e == 0) ? t[e] : lsum + t[e];
+            }
+            p = __builtin_convertvector(t, x8);
+        };
+        auto tile = [&](auto stage_tag, int j, f32x16 &s_cur, f32x16 &s_next) {
+            constexpr int P = decltype(stage_tag)::value;
+            constexpr int VOFF = P * STAGE_BYTES + TILE_BYTES;
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's copies for this step have landed
+            __syncthreads();                                    // ... every thread's; step j-1 is done everywhere
+            if (j + 2 < nt) issue_part(false, kbeg + (j + 2) * BC, P);
+            if (j + 1 < nt) issue_part(true, kbeg + (j + 1) * BC, P ^ 1);
+            if (!active_at(j)) return;  // wave-uniform; no later tile is active either
+            const int k0 = kbeg + j * BC;
+            const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > q0w);
+            if (need_mask) {
+                const int qrow = q0w + l32;
+                const int base = k0 + 4 * g;
+                int lim = Nk - 1 - base;
+                if constexpr (CAUSAL) lim = min(lim, qrow - base);
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (layout::acc_row(r, 0) > lim) s_cur[r] = -__builtin_inff();
+            }
+            // P against the held max (a wave's first tile gives inf or NaN
+            // sums there, which the test below sends to the exact step), in
+            // one block with the next tile's S^T chain.  After the wave's last
+            // active tile that chain reads whatever K stage P^1 holds (in
+            // bounds) and its result is never used.
+            x8 pf[2];
+            float lsum = 0.0f;
+            exp_half(s_cur, 0, m_held[0], lsum, pf[0]);
+            exp_half(s_cur, 1, m_held[0], lsum, pf[1]);
+            s_chain(Int<P ^ 1>{}, s_next, Int<7>{});
+            const float held = running_sum_bound<T>() ? l_part[0] + lsum : lsum;
+            if (__ballot(!(held <= held_sum_bound<T>())) != 0ull) {
+                float mx = -__builtin_inff();
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s_cur[r]);
+                mx = xor32_max(mx);
+                const float m_new = __builtin_fmaxf(m_held[0], mx * c);  // c > 0 (the sign is in Q)
+                const float alpha = (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_held[0] - m_new);
+                const bool held_any = __ballot(m_held[0] != -__builtin_inff()) != 0ull;
+                m_held[0] = m_new;
+                if (held_any) {
+                    l_part[0] *= alpha;
+                    const float alpha_hi = __shfl(alpha, (lane + 16) & 63);
+                    lt[0][0] *= alpha;
+                    lt[0][1] *= alpha_hi;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) oacc[0][db] *= alpha;
+                }
+                const float msub = (m_new == -__builtin_inff()) ? 0.0f : m_new;
+                exp_half(s_cur, 0, msub, lsum, pf[0]);
+                exp_half(s_cur, 1, msub, lsum, pf[1]);
+            }
+            l_part[0] += lsum;
+            // ---- O^T += V^T P^T, then lt += rowsum of the rounded P --------------
+            constexpr int NV = KS2 * DB;
+            constexpr int VPF = NV < 3 ? NV : 3;
+            auto read_v = [&](int i) {
+                const char *vb = smem + VOFF + voff[i % DB] + 16 * (i / DB) * ROW;
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4 *)(vb));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4 *)(vb + 8 * ROW));
+                return __builtin_bit_cast(x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            };
+            x8 vq[VPF];
+#pragma unroll
+            for (int i = 0; i < VPF; ++i) vq[i] = read_v(i);
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const x8 vf = vq[i % VPF];
+                if (i + VPF < NV) vq[i % VPF] = read_v(i + VPF);
+                oacc[0][i % DB] = M::run(vf, pf[i / DB], oacc[0][i % DB]);
+            }
+#pragma unroll
+            for (int ks2 = 0; ks2 < KS2; ++ks2) lt[0] = M::run16(ones8, pf[ks2], lt[0]);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * VPF, 0);
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (i + VPF < NV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, KS2, 0);
+        };
+        f32x16 sa, sb;
+        if (nt > 0) {  // the prologue's copies (K and V of tile 0, K of tile 1) have landed
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (active_at(0)) s_chain(Int<0>{}, sa, Int<0>{});
+        }
+        for (int j = 0; j < nt; j += 2) {
+            tile(Int<0>{}, j, sa, sb);
+            if (j + 1 < nt) tile(Int<1>{}, j + 1, sb, sa);
+        }
     }
 
     // ---- key split: merge the parts of each query group --------------------
@@ -714,7 +880,7 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(const in
     if (tid == 0) sched[0] = T < max_tiles ? T : max_tiles;  // only decreasing offsets can exceed the bound
 }
 
-template <typename T, int D, bool CAUSAL, int NW, int QW, int OCC, int BC = 64, int KSPLIT = 1>
+template <typename T, int D, bool CAUSAL, int NW, int QW, int OCC, int BC = 64, int KSPLIT = 1, bool PIPE = false>
 hipError_t launch_one(const PrefillArgs &base, bool varlen, int S, hipStream_t stream) {
     constexpr int BR = NW / KSPLIT * QW;
     PrefillArgs a = base;
@@ -734,11 +900,11 @@ hipError_t launch_one(const PrefillArgs &base, bool varlen, int S, hipStream_t s
         if (a.S > 1) {
             const long long nwg_split = nwg * a.S;
             if (nwg_split > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-            hipLaunchKernelGGL((prefill_kernel<T, D, CAUSAL, NW, QW, BC, OCC, kModeSplit>), dim3((unsigned)nwg_split),
+            hipLaunchKernelGGL((prefill_kernel<T, D, CAUSAL, NW, QW, BC, OCC, kModeSplit, 1, PIPE>), dim3((unsigned)nwg_split),
                                dim3(NW * 64), 0, stream, a);
             return hipGetLastError();
         }
-        hipLaunchKernelGGL((prefill_kernel<T, D, CAUSAL, NW, QW, BC, OCC, kModeDense>), dim3((unsigned)nwg),
+        hipLaunchKernelGGL((prefill_kernel<T, D, CAUSAL, NW, QW, BC, OCC, kModeDense, 1, PIPE>), dim3((unsigned)nwg),
                            dim3(NW * 64), 0, stream, a);
         return hipGetLastError();
     }
@@ -750,9 +916,18 @@ hipError_t launch_one(const PrefillArgs &base, bool varlen, int S, hipStream_t s
                        a.cu_k, S, a.total_q, a.total_k, (int)tiles, sched);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((prefill_kernel<T, D, CAUSAL, NW, QW, BC, OCC, kModeVarlen>), dim3((unsigned)nwg),
+    hipLaunchKernelGGL((prefill_kernel<T, D, CAUSAL, NW, QW, BC, OCC, kModeVarlen, 1, PIPE>), dim3((unsigned)nwg),
                        dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
+}
+
+// FA_PREFILL_PIPE=1 runs shape 3 with the pipelined schedule (next tile's
+// S^T chain beside this tile's softmax).  Its results are bit for bit those
+// of the default schedule; it needs 204 registers (two waves per SIMD, where
+// the default fits three) and measured 12-17% slower, so it is off by default.
+bool prefill_pipe() {
+    const char *env = getenv("FA_PREFILL_PIPE");
+    return env != nullptr && env[0] == '1' && env[1] == '\0';
 }
 
 template <typename T, int D, bool CAUSAL>
@@ -762,7 +937,10 @@ hipError_t launch_shape(int shape, const PrefillArgs &a, bool varlen, int S, hip
         case kShapeW4Q64: return launch_one<T, D, CAUSAL, 4, 64, 1>(a, varlen, S, stream);
         case kShapeW2Q64: return launch_one<T, D, CAUSAL, 2, 64, 1>(a, varlen, S, stream);
         case kShapeW4Q32B32:  // a 32-key tile of d = 32 is too small to split over 256 threads
-            if constexpr (D >= 64) return launch_one<T, D, CAUSAL, 4, 32, 3, 32>(a, varlen, S, stream);
+            if constexpr (D >= 64) {
+                if (prefill_pipe()) return launch_one<T, D, CAUSAL, 4, 32, 2, 32, 1, true>(a, varlen, S, stream);
+                return launch_one<T, D, CAUSAL, 4, 32, 3, 32>(a, varlen, S, stream);
+            }
             else return launch_one<T, D, CAUSAL, 4, 32, 2>(a, varlen, S, stream);
         // key splits: two steps of staged keys must fit 64 KB of LDS
         case kShapeW4Q32K2:
