@@ -78,11 +78,18 @@ def test_full_size_prefill_every_row(fa, name):
     compare(out, lse, ref_o, ref_l, w.dtype, name)
 
 
-@pytest.mark.parametrize("name,nrows", [("prefill_causal_bf16_b8h16_n4096_d128", 3000),
-                                        ("long_bf16_b1h32_n16384_d128_qsigma8", 1500)])
-def test_full_size_prefill_sampled_rows(fa, name, nrows):
+@pytest.mark.parametrize("name,nrows,seed", [("prefill_causal_bf16_b8h16_n4096_d128", 3000, None),
+                                             ("long_bf16_b1h32_n16384_d128_qsigma8", 1500, None),
+                                             ("long_bf16_b1h32_n16384_d128_qsigma8", 1500, 2004),
+                                             ("long_bf16_b1h32_n16384_d128_qsigma8", 1500, 3004)])
+def test_full_size_prefill_sampled_rows(fa, name, nrows, seed):
+    """The full-size workloads on a sample of rows; the long workload (score
+    spread 8x, the thinnest margin to the bound) also on two more seeds."""
+    import dataclasses
     w = fa_inputs.WORKLOADS[name]
-    note("case %s (sampled %d rows)" % (name, nrows))
+    if seed is not None:
+        w = dataclasses.replace(w, seed=seed)
+    note("case %s seed %d (sampled %d rows)" % (name, w.seed, nrows))
     q, k, v = fa_inputs.make_workload(w)
     qd, kd, vd = to_dev(q, k, v)
     out, lse = fa.fa_fwd(qd, kd, vd, scale=w.scale, causal=w.causal)
