@@ -62,7 +62,7 @@ _COMMON = ["io_aware_amd/csrc/fa_layout.h", "io_aware_amd/csrc/fa_device.h"]
 KERNEL_SOURCES = {
     "prefill": ["io_aware_amd/csrc/fa_prefill.hip"] + _COMMON,
     "f32": ["io_aware_amd/csrc/fa_f32.hip"],
-    "decode": ["io_aware_amd/csrc/fa_decode.hip"],
+    "decode": ["io_aware_amd/csrc/fa_decode.hip"] + _COMMON,
     "backward": ["io_aware_amd/csrc/fa_backward.hip"] + _COMMON,
     "fp8": ["io_aware_amd/csrc/fa_fp8.hip"] + _COMMON,
 }

@@ -30,6 +30,7 @@
 #include <stdint.h>
 
 #include "fa_internal.h"
+#include "fa_layout.h"
 
 namespace fa {
 namespace {
@@ -48,6 +49,7 @@ struct SplitArgs {
     const void *v;
     float *ws_o;    // [BH, S, D] normalised chunk outputs
     float *ws_lse;  // [BH, S] chunk logsumexp (natural log)
+    int BH;         // batch * heads
     int Nk;         // contiguous K/V: keys per (b, h)
     int S;
     int chunk;      // contiguous K/V: keys per chunk = ceil(Nk / S)
@@ -139,8 +141,11 @@ __global__ __launch_bounds__(kSplitThreads) void splitkv_partial_kernel(SplitArg
     const int tid = threadIdx.x;
     const int dc = tid % CH;
     const int kl = tid / CH;
-    const int bh = blockIdx.x / a.S;
-    const int cidx = blockIdx.x - bh * a.S;
+    // Workgroup w goes to XCD w % 8: with the grid a multiple of 8 each XCD
+    // streams whole heads, chunk after chunk (the prefill's order without
+    // the mask; 3-4% faster than consecutive chunks spread over the XCDs)
+    int bh, cidx;
+    layout::map_workgroup(blockIdx.x, a.BH, a.S, false, bh, cidx);
     int len = a.Nk, chunk = a.chunk, b = 0, h = 0;
     if (PAGED) {
         b = bh / a.H;
@@ -305,6 +310,7 @@ __global__ __launch_bounds__(256) void splitkv_combine_kernel(CombineArgs a) {
 template <typename T, int D, bool PAGED>
 hipError_t launch_splitkv_typed(const SplitArgs &base, void *out, float *lse, int BH, hipStream_t stream) {
     SplitArgs a = base;
+    a.BH = BH;
     float *ws_o = a.ws_o;
     float *ws_lse = ws_o + (size_t)BH * a.S * D;
     a.ws_lse = ws_lse;
