@@ -40,7 +40,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLn2d = 0.693147180559945309417f;
 constexpr float kLog2e = 1.442695040888963407360f;
 constexpr int kSplitThreads = 256;
-constexpr int kKeysPerRound = 8;   // U: keys per thread per round
+// U: keys per thread per round, whose K and V loads are all in flight
+// together.  d = 128: 16 (165 VGPRs, three waves per SIMD; 2.9% faster than
+// 8 on contiguous B16 H32 Nk8192 in the per-XCD head order, 1% slower on the
+// paged decode, which keeps it too so that both paths round alike and agree
+// bit for bit under an identity table).  Smaller head dims, whose rounds of
+// 256 / (d / 8) * U keys would outgrow common chunks: 8.
+template <int D>
+constexpr int keys_per_round() { return D >= 128 ? 16 : 8; }
 constexpr int kMaxSplits = 1024;
 
 struct SplitArgs {
@@ -131,7 +138,7 @@ __global__ __launch_bounds__(kSplitThreads) void splitkv_partial_kernel(SplitArg
     constexpr int NT = kSplitThreads;
     constexpr int CH = D / 8;   // lanes per key row (16 bytes each)
     constexpr int KL = NT / CH; // key lanes
-    constexpr int U = kKeysPerRound;
+    constexpr int U = keys_per_round<D>();
     static_assert(CH <= 64 && (CH & (CH - 1)) == 0, "row lanes must be a power of two within a wave");
 
     __shared__ float sm_m[KL];
